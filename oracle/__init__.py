@@ -1,0 +1,6 @@
+"""Float64 CPU oracle for the selective scan (S6). Test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The HIP library never does.
+"""
+from .s6 import decode, recurrence, scan_fwd, silu, softplus, state_update  # noqa: F401
