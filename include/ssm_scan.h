@@ -1,0 +1,153 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan (S6) library, libssm_scan.so.
+ *
+ * What is computed.  For every batch row b, channel d and state index n:
+ *
+ *     Delta_t = softplus(delta_t + dt_bias_d)
+ *     Abar_t  = exp(Delta_t * A_dn)                     zero-order hold of a diagonal A
+ *     h_t     = Abar_t * h_{t-1} + Delta_t * B_tn * x_t  first-order input term Bbar = Delta * B
+ *     y_t     = sum_n C_tn * h_tn + Dskip_d * x_t        readout of the updated state
+ *     out_t   = y_t * silu(z_t)                          (out_t = y_t when z is NULL)
+ *
+ * The recurrence and readout are the selective state-space layer of the pages
+ * "Mamba" (sections "Main Claim", "Scan View"), "Mamba Selective State-Space
+ * Module" ("Math Or Compute Schema") and "DL0170 Mamba Selective SSM vs
+ * Attention" ("Mathematical Formulation": zero-order hold of a negative
+ * diagonal A, simplified input term, Delta as an input-dependent forget gate).
+ * The pages leave the step-size map, the skip term and the gate function
+ * open; softplus(delta + dt_bias), Dskip * x and silu are the readings this
+ * library implements.
+ *
+ * Layout.  All tensors are dense, row-major, with no strides:
+ *     x, delta, z, y : (batch, L, D), D fastest              io dtype
+ *     B, C           : (batch, L, N), shared by all channels io dtype
+ *     A              : (D, N)                                 float32
+ *     Dskip, dt_bias : (D)                                    float32
+ *     h0, h_last, h  : (batch, D, N), N fastest               float32
+ * N must be 16.  io dtype is SSM_F32 (float) or SSM_BF16 (bfloat16 bit
+ * patterns, 16 bits each); bf16 outputs are rounded to nearest even.
+ *
+ * Memory and execution.  Every pointer is a DEVICE pointer on the current HIP
+ * device.  The caller owns every buffer, including the workspace; the
+ * library allocates no device memory and keeps no pointer after a call
+ * returns.  Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the
+ * null stream) and never synchronise; buffers must stay alive until the
+ * stream has run them.
+ *
+ * Errors.  Every entry point validates all of its arguments before it enqueues
+ * anything; on error nothing is enqueued, no output is touched, the return
+ * value is a negative ssm_status and ssm_last_error() describes it.  A failed
+ * kernel launch returns SSM_ERR_HIP.  Non-finite inputs are not errors: they
+ * propagate through the arithmetic.  A positive A is accepted and may
+ * overflow (the pages' A is negative).
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum {
+    SSM_F32 = 0,   /* float32 */
+    SSM_BF16 = 1   /* bfloat16 bit patterns */
+} ssm_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = -1,       /* a required pointer is NULL */
+    SSM_ERR_SHAPE = -2,      /* batch, L or D < 1, a size overflows, or a bad chunk length */
+    SSM_ERR_N = -3,          /* N != 16 */
+    SSM_ERR_DTYPE = -4,      /* unknown io dtype */
+    SSM_ERR_ALIGN = -5,      /* a pointer is not aligned as required below */
+    SSM_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than the query returns */
+    SSM_ERR_ALIAS = -7,      /* an output overlaps an input or another output */
+    SSM_ERR_HIP = -8         /* a HIP call or kernel launch failed */
+} ssm_status;
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next ssm_* call on the same thread. */
+const char* ssm_last_error(void);
+
+/*
+ * Workspace bytes that ssm_scan_fwd needs for this shape (0 when the sequence
+ * is processed in one chunk).  chunk_len as for ssm_scan_fwd.  Returns a
+ * negative ssm_status for an invalid shape.  Host-only; touches no device.
+ */
+int64_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                     int io_dtype, int64_t chunk_len);
+
+/*
+ * Chunk plan used for this shape: writes the chunk length and chunk count
+ * (either pointer may be NULL).  Host-only.  Returns SSM_OK or a negative
+ * ssm_status.
+ */
+int ssm_scan_fwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                      int64_t chunk_len, int64_t* chunk_len_out, int64_t* n_chunks_out);
+
+/*
+ * Whole-sequence selective scan: out (into y) and the final state h_L.
+ *
+ * The sequence is cut into chunks of chunk_len tokens ("Mamba", "Scan View":
+ * the recurrence is associative, so chunks can be scanned in parallel and
+ * joined).  Each chunk first runs a local scan from a zero state to get its
+ * carry (summed step size, end state); the carries are then folded in order
+ * from h0 with (S1, H1) then (S2, H2) = (S1 + S2, exp(A * S2) * H1 + H2); a
+ * final pass rescans every chunk from its true starting state and writes y.
+ * The (batch, L, D, N) states never reach memory.
+ *
+ *   x, delta, B, C  required; z NULL = ungated; h0 NULL = zero initial state.
+ *   A, Dskip, dt_bias required.
+ *   y               required output, (batch, L, D) io dtype.
+ *   h_last          NULL = not wanted, else (batch, D, N) float32 output.
+ *   chunk_len       0 = the library's plan for the MI355X; else a positive
+ *                   multiple of 32 (a smaller, ragged last chunk is allowed).
+ *   workspace       at least ssm_scan_fwd_workspace_bytes(...) bytes, 16-byte
+ *                   aligned; may be NULL when that size is 0.
+ * Alignment: io tensors to their element size; B and C to 16 bytes; float32
+ * tensors to 4 bytes.  y and h_last must not overlap any input, each other or
+ * the workspace.
+ */
+int ssm_scan_fwd(const void* x, const void* delta, const void* z,
+                 const void* B, const void* C,
+                 const float* A, const float* Dskip, const float* dt_bias,
+                 const float* h0,
+                 void* y, float* h_last,
+                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                 int64_t chunk_len, void* workspace, int64_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Single-token decode step against a cached float32 state, in place.
+ *
+ * The recurrence advanced by one token ("Mamba & State-Space Sequence
+ * Models", "Core mechanics": inference runs the recurrence one step at a
+ * time with a state whose size does not grow): h <- Abar * h + Delta * B * x,
+ * then out = (C . h + Dskip * x) * silu(z).
+ *
+ *   h               (batch, D, N) float32, read and overwritten.
+ *   x, delta, z     (batch, D) io dtype; z NULL = ungated.
+ *   B, C            (batch, N) io dtype.
+ *   y               (batch, D) io dtype output; must not overlap h or any input.
+ */
+int ssm_state_update(float* h,
+                     const void* x, const void* delta, const void* z,
+                     const void* B, const void* C,
+                     const float* A, const float* Dskip, const float* dt_bias,
+                     void* y,
+                     int64_t batch, int64_t D, int64_t N, int io_dtype,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

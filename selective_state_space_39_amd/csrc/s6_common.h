@@ -1,0 +1,87 @@
+// Shared device helpers and launcher declarations for the gfx950 selective scan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s6 {
+
+constexpr int kN = 16;          // state size (Mamba-1)
+constexpr int kWave = 64;       // CDNA wavefront
+constexpr int kBlock = 256;     // 4 waves per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// io element access: float32, or bfloat16 carried as 16-bit patterns
+// ---------------------------------------------------------------------------
+struct F32 {
+    using T = float;
+    static __device__ __forceinline__ float load(const float* p, uint32_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, uint32_t i, float v) { p[i] = v; }
+};
+
+struct BF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const uint16_t* p, uint32_t i) {
+        return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);   // exact widening
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, uint32_t i, float v) {
+        __bf16 b = static_cast<__bf16>(v);                            // round to nearest even
+        p[i] = __builtin_bit_cast(uint16_t, b);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// elementwise maps
+// ---------------------------------------------------------------------------
+
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)).  log1p(e) is taken as
+// log(u) + (e - (u - 1)) with u = fl(1 + e): the second term restores the
+// part of e that rounding 1 + e dropped, which matters for small steps.
+__device__ __forceinline__ float softplus(float v) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+    const float u = 1.0f + e;
+    const float lost = e - (u - 1.0f);
+    return fmaxf(v, 0.0f) + fmaf(__builtin_amdgcn_logf(u), kLn2, lost);
+}
+
+// silu(z) = z / (1 + exp(-z)); exp overflow gives 1/inf = 0 and a signed zero.
+__device__ __forceinline__ float silu(float z) {
+    const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+}  // namespace s6
+
+// ---------------------------------------------------------------------------
+// launchers (host side, defined in s6_kernels.hip)
+// ---------------------------------------------------------------------------
+struct S6ScanArgs {
+    const void* x; const void* delta; const void* z;
+    const void* B; const void* C;
+    const float* A; const float* Dskip; const float* dt_bias;
+    const float* h0;
+    void* y; float* h_last;
+    float* carry_S;    // (batch, n_chunks - 1, D)
+    float* carry_H;    // (batch, n_chunks - 1, N, D)
+    int64_t batch, L, D;
+    int64_t chunk_len, n_chunks;
+    int bf16;
+};
+
+struct S6StepArgs {
+    float* h;
+    const void* x; const void* delta; const void* z;
+    const void* B; const void* C;
+    const float* A; const float* Dskip; const float* dt_bias;
+    void* y;
+    int64_t batch, D;
+    int bf16;
+};
+
+hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream);
+hipError_t s6_launch_step(const S6StepArgs& a, hipStream_t stream);

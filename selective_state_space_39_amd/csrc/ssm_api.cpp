@@ -1,0 +1,244 @@
+// C ABI of libssm_scan.so: argument validation, chunk plan, workspace layout,
+// error reporting, launches.  Declared in include/ssm_scan.h.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "s6_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return SSM_OK;
+}
+
+constexpr int64_t kN = 16;
+constexpr int64_t kChunkAlign = 32;
+constexpr int64_t kMaxGrid = 65535;              // grid y (chunks) and z (batch rows)
+constexpr int64_t kMaxBytes = int64_t(1) << 60;  // any single tensor
+// Output wavefronts the automatic plan aims for: two per SIMD of the 256-CU MI355X.
+constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kMinChunk = 64;
+
+int64_t esize(int io) { return io == SSM_BF16 ? 2 : 4; }
+
+// a*b without overflow beyond kMaxBytes; -1 on overflow
+int64_t mul_ck(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a != 0 && b > kMaxBytes / a) return -1;
+    return a * b;
+}
+
+struct Range {
+    const char* name;
+    uintptr_t lo;
+    uintptr_t hi;   // exclusive
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.lo || !b.lo || a.hi == a.lo || b.hi == b.lo) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+    uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    return Range{name, u, u ? u + static_cast<uintptr_t>(bytes) : 0};
+}
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Plan {
+    int64_t chunk_len;
+    int64_t n_chunks;
+    int64_t ws_bytes;
+};
+
+int check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, int io) {
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown io dtype %d (0 = f32, 1 = bf16)", io);
+    if (N != kN) return fail(SSM_ERR_N, "N = %lld: this library is built for N = 16", (long long)N);
+    if (batch < 1 || L < 1 || D < 1)
+        return fail(SSM_ERR_SHAPE, "batch, L and D must be >= 1 (got %lld, %lld, %lld)",
+                    (long long)batch, (long long)L, (long long)D);
+    if (batch > kMaxGrid) return fail(SSM_ERR_SHAPE, "batch = %lld exceeds %lld", (long long)batch, (long long)kMaxGrid);
+    if (D > (int64_t(1) << 30)) return fail(SSM_ERR_SHAPE, "D = %lld is too large", (long long)D);
+    if (L > (int64_t(1) << 30)) return fail(SSM_ERR_SHAPE, "L = %lld is too large", (long long)L);
+    int64_t e = mul_ck(mul_ck(mul_ck(batch, L), D), 4);
+    int64_t s = mul_ck(mul_ck(mul_ck(batch, L), kN), 4);
+    if (e < 0 || s < 0) return fail(SSM_ERR_SHAPE, "batch * L * D overflows");
+    return SSM_OK;
+}
+
+int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
+    if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
+        return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
+                    (long long)chunk_len, (long long)kChunkAlign);
+    if (chunk_len == 0) {
+        const int64_t groups = batch * ((D + 63) / 64);
+        int64_t want = (kTargetWaves + groups - 1) / groups;
+        const int64_t cap = (L + kMinChunk - 1) / kMinChunk;
+        if (want > cap) want = cap;
+        if (want < 1) want = 1;
+        int64_t len = (L + want - 1) / want;
+        len = (len + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        chunk_len = len;
+    }
+    p.chunk_len = chunk_len;
+    p.n_chunks = (L + chunk_len - 1) / chunk_len;
+    if (p.n_chunks > kMaxGrid)
+        return fail(SSM_ERR_SHAPE, "%lld chunks exceed %lld; use a longer chunk_len",
+                    (long long)p.n_chunks, (long long)kMaxGrid);
+    const int64_t carries = mul_ck(mul_ck(batch, p.n_chunks - 1), D);
+    if (carries < 0) return fail(SSM_ERR_SHAPE, "workspace size overflows");
+    // carry_S (batch, n-1, D) then carry_H (batch, n-1, N, D), float32, 256-byte aligned parts
+    const int64_t sb = (carries * 4 + 255) / 256 * 256;
+    p.ws_bytes = (p.n_chunks > 1) ? sb + carries * kN * 4 : 0;
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_last_error(void) { return g_err.c_str(); }
+
+int64_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                                     int64_t chunk_len) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    Plan p;
+    rc = make_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+    ok();
+    return p.ws_bytes;
+}
+
+int ssm_scan_fwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype, int64_t chunk_len,
+                      int64_t* chunk_len_out, int64_t* n_chunks_out) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    Plan p;
+    rc = make_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+    if (chunk_len_out) *chunk_len_out = p.chunk_len;
+    if (n_chunks_out) *n_chunks_out = p.n_chunks;
+    return ok();
+}
+
+int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                 const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                 void* y, float* h_last,
+                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                 int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    Plan p;
+    rc = make_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+
+    struct { const void* p; const char* n; } req[] = {
+        {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
+        {dt_bias, "dt_bias"}, {y, "y"}};
+    for (auto& r : req)
+        if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    if (p.ws_bytes > 0) {
+        if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)p.ws_bytes);
+        if (workspace_bytes < p.ws_bytes)
+            return fail(SSM_ERR_WORKSPACE, "workspace has %lld bytes; %lld needed",
+                        (long long)workspace_bytes, (long long)p.ws_bytes);
+    }
+
+    const int64_t es = esize(io_dtype);
+    struct { const void* p; int64_t a; const char* n; } al[] = {
+        {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {B, 16, "B"}, {C, 16, "C"}, {y, es, "y"},
+        {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 4, "h0"}, {h_last, 4, "h_last"},
+        {workspace, 16, "workspace"}};
+    for (auto& r : al)
+        if (r.p && !aligned(r.p, r.a))
+            return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
+
+    const int64_t seq = batch * L * D * es, bc = batch * L * kN * es, st = batch * D * kN * 4;
+    const Range ins[] = {rng("x", x, seq), rng("delta", delta, seq), rng("z", z, seq), rng("B", B, bc),
+                         rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
+                         rng("dt_bias", dt_bias, D * 4), rng("h0", h0, st),
+                         rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes)};
+    const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st)};
+    for (auto& o : outs)
+        for (auto& i : ins)
+            if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
+    if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+
+    S6ScanArgs a{};
+    a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.y = y; a.h_last = h_last;
+    if (p.ws_bytes > 0) {
+        const int64_t carries = batch * (p.n_chunks - 1) * D;
+        a.carry_S = static_cast<float*>(workspace);
+        a.carry_H = reinterpret_cast<float*>(static_cast<char*>(workspace) + (carries * 4 + 255) / 256 * 256);
+    }
+    a.batch = batch; a.L = L; a.D = D;
+    a.chunk_len = p.chunk_len; a.n_chunks = p.n_chunks;
+    a.bf16 = io_dtype == SSM_BF16;
+    hipError_t e = s6_launch_scan(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int ssm_state_update(float* h, const void* x, const void* delta, const void* z, const void* B, const void* C,
+                     const float* A, const float* Dskip, const float* dt_bias, void* y,
+                     int64_t batch, int64_t D, int64_t N, int io_dtype, void* stream) {
+    int rc = check_shape(batch, 1, D, N, io_dtype);
+    if (rc) return rc;
+    struct { const void* p; const char* n; } req[] = {
+        {h, "h"}, {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
+        {dt_bias, "dt_bias"}, {y, "y"}};
+    for (auto& r : req)
+        if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    const int64_t es = esize(io_dtype);
+    struct { const void* p; int64_t a; const char* n; } al[] = {
+        {h, 16, "h"}, {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {B, es, "B"}, {C, es, "C"},
+        {y, es, "y"}, {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}};
+    for (auto& r : al)
+        if (r.p && !aligned(r.p, r.a))
+            return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
+    const int64_t tok = batch * D * es, bc = batch * kN * es, st = batch * D * kN * 4;
+    const Range ins[] = {rng("x", x, tok), rng("delta", delta, tok), rng("z", z, tok), rng("B", B, bc),
+                         rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
+                         rng("dt_bias", dt_bias, D * 4)};
+    const Range hs = rng("h", h, st), ys = rng("y", y, tok);
+    for (auto& i : ins) {
+        if (overlap(hs, i)) return fail(SSM_ERR_ALIAS, "h overlaps %s", i.name);
+        if (overlap(ys, i)) return fail(SSM_ERR_ALIAS, "y overlaps %s", i.name);
+    }
+    if (overlap(hs, ys)) return fail(SSM_ERR_ALIAS, "y overlaps h");
+
+    S6StepArgs a{};
+    a.h = h; a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y;
+    a.batch = batch; a.D = D; a.bf16 = io_dtype == SSM_BF16;
+    hipError_t e = s6_launch_step(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"
