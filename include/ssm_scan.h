@@ -146,6 +146,22 @@ int ssm_state_update(float* h,
                      int64_t batch, int64_t D, int64_t N, int io_dtype,
                      void* stream);
 
+/*
+ * Per-kernel timing, for measurement tools; not needed to compute anything.
+ *
+ * ssm_timing_enable(1) makes every later kernel launch of this library (on
+ * any thread) bracketed by two hipEvents recorded on the launch's own stream;
+ * ssm_timing_enable(0) stops recording.  Returns SSM_OK or SSM_ERR_HIP.
+ *
+ * ssm_timing_collect waits for every recorded event, then writes for up to
+ * max_kernels distinct kernels their name (static strings owned by the
+ * library), launch count and summed duration in milliseconds, clears the
+ * record and returns the number of distinct kernels (negative ssm_status on a
+ * HIP error).  Any output pointer may be NULL.
+ */
+int ssm_timing_enable(int on);
+int ssm_timing_collect(int max_kernels, const char** names, int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,11 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_state_update.restype = i32
     L.ssm_state_update.argtypes = [vp] * 10 + [i64, i64, i64, i32, vp]
+    L.ssm_timing_enable.restype = i32
+    L.ssm_timing_enable.argtypes = [i32]
+    L.ssm_timing_collect.restype = i32
+    L.ssm_timing_collect.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
+                                     ctypes.POINTER(ctypes.c_double)]
     if L.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH} has ABI {L.ssm_abi_version()}, expected {ABI_VERSION}")
     _lib = L
@@ -171,3 +176,19 @@ def state_update(h, x, delta, A, B, C, D, dt_bias, z=None, out=None):
                                 _ptr(dt_bias), _ptr(y), batch, Dc, N_STATE, io, _stream(dev))
     _check(rc)
     return y
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every later library kernel launch with HIP events on its stream."""
+    _check(lib().ssm_timing_enable(1 if on else 0))
+
+
+def timing_collect(max_kernels: int = 16) -> dict:
+    """{kernel name: (launches, total ms)} recorded since the last collect (waits for the events)."""
+    names = (ctypes.c_char_p * max_kernels)()
+    cnt = (ctypes.c_int64 * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    n = lib().ssm_timing_collect(max_kernels, names, cnt, ms)
+    if n < 0:
+        _check(n)
+    return {names[i].decode(): (int(cnt[i]), float(ms[i])) for i in range(min(n, max_kernels))}

@@ -83,5 +83,9 @@ struct S6StepArgs {
     int bf16;
 };
 
+// Optional per-launch timing (ssm_timing_enable): called before and after
+// every kernel launch with the launch's stream.
+void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin);
+
 hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream);
 hipError_t s6_launch_step(const S6StepArgs& a, hipStream_t stream);

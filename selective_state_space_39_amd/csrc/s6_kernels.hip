@@ -299,10 +299,14 @@ static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
     const unsigned gx = static_cast<unsigned>((a.D + kBlock - 1) / kBlock);
     if (a.n_chunks > 1) {
         dim3 g1(gx, static_cast<unsigned>(a.n_chunks - 1), static_cast<unsigned>(a.batch));
+        s6_timing_mark("s6_chunk_carry", stream, true);
         hipLaunchKernelGGL(s6_chunk_carry<IO>, g1, dim3(kBlock), 0, stream, a);
+        s6_timing_mark("s6_chunk_carry", stream, false);
     }
     dim3 g3(gx, static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(a.batch));
+    s6_timing_mark("s6_chunk_out", stream, true);
     hipLaunchKernelGGL((s6_chunk_out<IO, GATED>), g3, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_chunk_out", stream, false);
     return hipGetLastError();
 }
 
@@ -316,7 +320,9 @@ template <class IO, bool GATED>
 static hipError_t launch_step_t(const S6StepArgs& a, hipStream_t stream) {
     dim3 g(static_cast<unsigned>((a.D + kBlock / 4 - 1) / (kBlock / 4)),
            static_cast<unsigned>((a.batch + kStepRows - 1) / kStepRows));
+    s6_timing_mark("s6_step", stream, true);
     hipLaunchKernelGGL((s6_step<IO, GATED>), g, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_step", stream, false);
     return hipGetLastError();
 }
 

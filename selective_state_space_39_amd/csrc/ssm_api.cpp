@@ -4,10 +4,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "s6_common.h"
 
@@ -113,9 +117,91 @@ int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
     return SSM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// per-kernel timing
+// ---------------------------------------------------------------------------
+struct TimingRec {
+    const char* kernel;
+    hipEvent_t begin, end;
+};
+
+std::atomic<bool> g_timing{false};
+std::mutex g_timing_mu;
+std::vector<TimingRec> g_recs;           // completed pairs
+std::vector<hipEvent_t> g_pool;          // reusable events
+thread_local hipEvent_t t_open = nullptr;
+thread_local const char* t_open_name = nullptr;
+
+hipEvent_t take_event() {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
 }  // namespace
 
+void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin) {
+    if (!g_timing.load(std::memory_order_relaxed)) return;
+    hipEvent_t e = take_event();
+    if (!e) return;
+    if (hipEventRecord(e, stream) != hipSuccess) return;
+    if (begin) {
+        t_open = e;
+        t_open_name = kernel;
+    } else if (t_open && t_open_name == kernel) {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        g_recs.push_back(TimingRec{kernel, t_open, e});
+        t_open = nullptr;
+    }
+}
+
 extern "C" {
+
+int ssm_timing_enable(int on) {
+    g_timing.store(on != 0);
+    return ok();
+}
+
+int ssm_timing_collect(int max_kernels, const char** names, int64_t* launches, double* total_ms) {
+    std::vector<TimingRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        recs.swap(g_recs);
+    }
+    std::vector<const char*> kn;
+    std::vector<int64_t> cnt;
+    std::vector<double> ms;
+    int status = SSM_OK;
+    for (auto& r : recs) {
+        if (hipEventSynchronize(r.end) != hipSuccess) status = SSM_ERR_HIP;
+        float t = 0.0f;
+        if (status == SSM_OK && hipEventElapsedTime(&t, r.begin, r.end) != hipSuccess) status = SSM_ERR_HIP;
+        size_t i = 0;
+        while (i < kn.size() && std::strcmp(kn[i], r.kernel) != 0) ++i;
+        if (i == kn.size()) { kn.push_back(r.kernel); cnt.push_back(0); ms.push_back(0.0); }
+        cnt[i] += 1;
+        ms[i] += t;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        for (auto& r : recs) { g_pool.push_back(r.begin); g_pool.push_back(r.end); }
+    }
+    if (status != SSM_OK) return fail(status, "timing events failed: %s", hipGetErrorString(hipGetLastError()));
+    for (int i = 0; i < static_cast<int>(kn.size()) && i < max_kernels; ++i) {
+        if (names) names[i] = kn[i];
+        if (launches) launches[i] = cnt[i];
+        if (total_ms) total_ms[i] = ms[i];
+    }
+    ok();
+    return static_cast<int>(kn.size());
+}
+
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
