@@ -149,9 +149,13 @@ int ssm_state_update(float* h,
 /*
  * Per-kernel timing, for measurement tools; not needed to compute anything.
  *
- * ssm_timing_enable(1) makes every later kernel launch of this library (on
- * any thread) bracketed by two hipEvents recorded on the launch's own stream;
- * ssm_timing_enable(0) stops recording.  Returns SSM_OK or SSM_ERR_HIP.
+ * ssm_timing_enable(1, kernel) makes every later launch of the named kernel
+ * of this library (every kernel when kernel is NULL), on any thread,
+ * bracketed by two hipEvents recorded on the launch's own stream;
+ * ssm_timing_enable(0, NULL) stops recording.  Recording events between
+ * kernels costs time, so time whole calls with recording off.  Kernel names:
+ * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step".  Returns
+ * SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the
@@ -159,7 +163,7 @@ int ssm_state_update(float* h,
  * record and returns the number of distinct kernels (negative ssm_status on a
  * HIP error).  Any output pointer may be NULL.
  */
-int ssm_timing_enable(int on);
+int ssm_timing_enable(int on, const char* kernel);
 int ssm_timing_collect(int max_kernels, const char** names, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus

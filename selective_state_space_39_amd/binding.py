@@ -50,7 +50,7 @@ def lib() -> ctypes.CDLL:
     L.ssm_state_update.restype = i32
     L.ssm_state_update.argtypes = [vp] * 10 + [i64, i64, i64, i32, vp]
     L.ssm_timing_enable.restype = i32
-    L.ssm_timing_enable.argtypes = [i32]
+    L.ssm_timing_enable.argtypes = [i32, ctypes.c_char_p]
     L.ssm_timing_collect.restype = i32
     L.ssm_timing_collect.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
                                      ctypes.POINTER(ctypes.c_double)]
@@ -178,9 +178,9 @@ def state_update(h, x, delta, A, B, C, D, dt_bias, z=None, out=None):
     return y
 
 
-def timing_enable(on: bool = True) -> None:
-    """Bracket every later library kernel launch with HIP events on its stream."""
-    _check(lib().ssm_timing_enable(1 if on else 0))
+def timing_enable(on: bool = True, kernel: Optional[str] = None) -> None:
+    """Bracket later launches of `kernel` (every kernel if None) with HIP events on their stream."""
+    _check(lib().ssm_timing_enable(1 if on else 0, kernel.encode() if (on and kernel) else None))
 
 
 def timing_collect(max_kernels: int = 16) -> dict:

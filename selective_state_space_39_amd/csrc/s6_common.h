@@ -71,6 +71,7 @@ struct S6ScanArgs {
     int64_t batch, L, D;
     int64_t chunk_len, n_chunks;
     int bf16;
+    int pair_loads;    // bf16 with D even and x, delta, z 4-byte aligned: dword loads
 };
 
 struct S6StepArgs {

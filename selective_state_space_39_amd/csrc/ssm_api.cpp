@@ -38,8 +38,6 @@ constexpr int64_t kN = 16;
 constexpr int64_t kChunkAlign = 32;
 constexpr int64_t kMaxGrid = 65535;              // grid y (chunks) and z (batch rows)
 constexpr int64_t kMaxBytes = int64_t(1) << 60;  // any single tensor
-// Output wavefronts the automatic plan aims for: two per SIMD of the 256-CU MI355X.
-constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kMinChunk = 64;
 
 int64_t esize(int io) { return io == SSM_BF16 ? 2 : 4; }
@@ -90,25 +88,54 @@ int check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, int io) {
     return SSM_OK;
 }
 
+// Cost model of the MI355X (1024 SIMDs) used by the automatic plan, in units
+// of one wavefront-token (64 channels x 16 states advanced by one token):
+// with w waves resident on a SIMD, a SIMD finishes w of them per unit, but a
+// lone wave runs at ~1/1.31 of that (measured: it cannot hide its own
+// latencies); a carry token costs ~0.74 of an output token; every extra
+// launch costs ~14 units (~4 us).  A plan is a chunk length; the estimate is
+// (waves per SIMD, rounded up) x (tokens per chunk) for each of the two passes.
+constexpr int64_t kSimds = 1024;
+
+double est_pass(int64_t waves, int64_t tokens, double per_token) {
+    if (waves <= 0) return 0.0;
+    const int64_t w = (waves + kSimds - 1) / kSimds;
+    const double lone = (waves < kSimds && w == 1) ? 1.31 : 1.0;
+    return static_cast<double>(w) * static_cast<double>(tokens) * per_token * lone;
+}
+
+double est_plan(int64_t groups, int64_t L, int64_t len) {
+    const int64_t n = (L + len - 1) / len;
+    double t = est_pass(groups * n, len, 1.0);
+    if (n > 1) t += est_pass(groups * (n - 1), len, 0.74) + 14.0 + 0.05 * static_cast<double>(n);
+    return t;
+}
+
 int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
     if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
         return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
                     (long long)chunk_len, (long long)kChunkAlign);
     if (chunk_len == 0) {
+        // waves per chunk: one per 64 channels of each batch row
         const int64_t groups = batch * ((D + 63) / 64);
-        int64_t want = (kTargetWaves + groups - 1) / groups;
-        const int64_t cap = (L + kMinChunk - 1) / kMinChunk;
-        if (want > cap) want = cap;
-        if (want < 1) want = 1;
-        int64_t len = (L + want - 1) / want;
-        len = (len + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-        chunk_len = len;
+        const int64_t whole = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        int64_t best = whole;
+        double best_t = est_plan(groups, L, whole);
+        for (int64_t len = whole - kChunkAlign; len >= kMinChunk; len -= kChunkAlign) {
+            if ((L + len - 1) / len > kMaxGrid) break;
+            const double t = est_plan(groups, L, len);
+            if (t < best_t * 0.999) { best_t = t; best = len; }
+        }
+        chunk_len = best;
     }
     p.chunk_len = chunk_len;
     p.n_chunks = (L + chunk_len - 1) / chunk_len;
     if (p.n_chunks > kMaxGrid)
         return fail(SSM_ERR_SHAPE, "%lld chunks exceed %lld; use a longer chunk_len",
                     (long long)p.n_chunks, (long long)kMaxGrid);
+    // one workgroup per (256-channel block, batch row, chunk) in a 1-D grid
+    if (batch * ((D + 255) / 256) * p.n_chunks > (int64_t(1) << 31) - 1)
+        return fail(SSM_ERR_SHAPE, "batch * ceil(D / 256) * chunks exceeds the grid limit");
     const int64_t carries = mul_ck(mul_ck(batch, p.n_chunks - 1), D);
     if (carries < 0) return fail(SSM_ERR_SHAPE, "workspace size overflows");
     // carry_S (batch, n-1, D) then carry_H (batch, n-1, N, D), float32, 256-byte aligned parts
@@ -126,6 +153,7 @@ struct TimingRec {
 };
 
 std::atomic<bool> g_timing{false};
+std::string g_timing_only;               // empty: every kernel
 std::mutex g_timing_mu;
 std::vector<TimingRec> g_recs;           // completed pairs
 std::vector<hipEvent_t> g_pool;          // reusable events
@@ -148,6 +176,10 @@ hipEvent_t take_event() {
 
 void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin) {
     if (!g_timing.load(std::memory_order_relaxed)) return;
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        if (!g_timing_only.empty() && g_timing_only != kernel) return;
+    }
     hipEvent_t e = take_event();
     if (!e) return;
     if (hipEventRecord(e, stream) != hipSuccess) return;
@@ -163,7 +195,11 @@ void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin) {
 
 extern "C" {
 
-int ssm_timing_enable(int on) {
+int ssm_timing_enable(int on, const char* kernel) {
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        g_timing_only = (on && kernel) ? kernel : "";
+    }
     g_timing.store(on != 0);
     return ok();
 }
@@ -285,6 +321,7 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
     a.batch = batch; a.L = L; a.D = D;
     a.chunk_len = p.chunk_len; a.n_chunks = p.n_chunks;
     a.bf16 = io_dtype == SSM_BF16;
+    a.pair_loads = a.bf16 && D % 2 == 0 && aligned(x, 4) && aligned(delta, 4) && (!z || aligned(z, 4));
     hipError_t e = s6_launch_scan(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
