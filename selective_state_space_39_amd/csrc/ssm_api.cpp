@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdint>
@@ -88,26 +89,33 @@ int check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, int io) {
     return SSM_OK;
 }
 
-// Cost model of the MI355X (1024 SIMDs) used by the automatic plan, in units
-// of one wavefront-token (64 channels x 16 states advanced by one token):
-// with w waves resident on a SIMD, a SIMD finishes w of them per unit, but a
-// lone wave runs at ~1/1.31 of that (measured: it cannot hide its own
-// latencies); a carry token costs ~0.74 of an output token; every extra
-// launch costs ~14 units (~4 us).  A plan is a chunk length; the estimate is
-// (waves per SIMD, rounded up) x (tokens per chunk) for each of the two passes.
+// Cost model of the MI355X (1024 SIMDs) used by the automatic plan, fitted to
+// measured kernel times (us, bf16 io, N = 16).  A pass with W wavefronts puts
+// w = ceil(W / 1024) on each SIMD, and its makespan is w x (tokens per chunk)
+// x (time per wavefront-token at w waves per SIMD): a lone wave cannot hide
+// its own latencies, and from about four waves per SIMD the VALU stays busy.
+// The carry scan costs ~4 us plus a per-carry term set by its traffic (or by
+// its latency when there are few channels); every extra launch ~4 us.
 constexpr int64_t kSimds = 1024;
+constexpr double kOutUs[7] = {0.0, 0.36, 0.241, 0.235, 0.206, 0.200, 0.192};   // by waves per SIMD
+constexpr double kCarryUs[7] = {0.0, 0.30, 0.211, 0.198, 0.169, 0.165, 0.157};
 
-double est_pass(int64_t waves, int64_t tokens, double per_token) {
+constexpr double kWaveSetupTokens = 6.0;     // per-wavefront prologue, in token equivalents
+
+double est_pass(int64_t waves, int64_t tokens, const double* per_token) {
     if (waves <= 0) return 0.0;
     const int64_t w = (waves + kSimds - 1) / kSimds;
-    const double lone = (waves < kSimds && w == 1) ? 1.31 : 1.0;
-    return static_cast<double>(w) * static_cast<double>(tokens) * per_token * lone;
+    return static_cast<double>(w) * (static_cast<double>(tokens) + kWaveSetupTokens) * per_token[w < 6 ? w : 6];
 }
 
-double est_plan(int64_t groups, int64_t L, int64_t len) {
+double est_plan(int64_t batch, int64_t D, int64_t L, int64_t len) {
+    const int64_t groups = batch * ((D + 63) / 64);      // wavefronts per chunk
     const int64_t n = (L + len - 1) / len;
-    double t = est_pass(groups * n, len, 1.0);
-    if (n > 1) t += est_pass(groups * (n - 1), len, 0.74) + 14.0 + 0.05 * static_cast<double>(n);
+    double t = est_pass(groups * n, len, kOutUs);
+    if (n > 1) {
+        const double per_carry = std::max(static_cast<double>(batch * D) * 2.4e-5, 0.12);
+        t += est_pass(groups * (n - 1), len, kCarryUs) + 4.0 + per_carry * static_cast<double>(n - 1) + 8.0;
+    }
     return t;
 }
 
@@ -116,14 +124,12 @@ int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
         return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
                     (long long)chunk_len, (long long)kChunkAlign);
     if (chunk_len == 0) {
-        // waves per chunk: one per 64 channels of each batch row
-        const int64_t groups = batch * ((D + 63) / 64);
         const int64_t whole = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
         int64_t best = whole;
-        double best_t = est_plan(groups, L, whole);
+        double best_t = est_plan(batch, D, L, whole);
         for (int64_t len = whole - kChunkAlign; len >= kMinChunk; len -= kChunkAlign) {
             if ((L + len - 1) / len > kMaxGrid) break;
-            const double t = est_plan(groups, L, len);
+            const double t = est_plan(batch, D, L, len);
             if (t < best_t * 0.999) { best_t = t; best = len; }
         }
         chunk_len = best;
