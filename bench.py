@@ -44,7 +44,7 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12        # 78.64, fp32 vector without packed math
 SLOTS_PER_ELEMENT = 112
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
-WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4}
+WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5}
 KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/s6_kernels.hip",
                   "selective_state_space_39_amd/csrc/s6_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -76,6 +76,56 @@ def measured_traffic(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
+CALIB_BYTES = 256 << 20           # copy-kernel calibration size
+CALIB_REPS = 3
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, for FETCH_SIZE / WRITE_SIZE calibration."""
+    import torch
+    a = torch.ones(CALIB_BYTES // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(CALIB_REPS):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": CALIB_BYTES, "reps": CALIB_REPS}))
+
+
+def _pmc(path, counter, name_part):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {name_part!r} in {path}")
+    return sum(vals) / len(vals)
+
+
+def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv):
+    """HBM bytes per launch of each library kernel from rocprofv3 --pmc runs (KiB per dispatch),
+    each counter scaled by what it reads for the copy kernel of known size."""
+    f_cal = CALIB_BYTES / 1024 / _pmc(calib_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    w_cal = CALIB_BYTES / 1024 / _pmc(calib_write_csv, "WRITE_SIZE", "copyBuffer")
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        t = {}
+    rec = {}
+    for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step"):
+        try:
+            fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
+        except SystemExit:
+            continue
+        rec[kname] = {"bytes_per_launch": round((fk * f_cal + wk * w_cal) * 1024),
+                      "fetch_kib_raw": fk, "write_kib_raw": wk, "source_hash": kernel_source_hash()}
+    t[workload] = rec
+    t["_calibration"] = {"fetch_factor": round(f_cal, 4), "write_factor": round(w_cal, 4),
+                         "copy_bytes": CALIB_BYTES}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+    print(json.dumps(t[workload]))
+
+
 def cpu_baseline(s, min_seconds=10.0, max_passes=3):
     """The float64 oracle as it stands, on the host, over whole passes of the workload."""
     import numpy as np
@@ -98,6 +148,77 @@ def cpu_baseline(s, min_seconds=10.0, max_passes=3):
                       f"NumPy float64 elementwise loop, single-threaded (BLAS pool {blas_threads} unused)"}
 
 
+def decode_bytes(batch, D, N=16, io_bytes=2):
+    """State read and written; x, delta, z read and y written; B, C read; A, Dskip, dt_bias read."""
+    return batch * D * (2 * N * 4 + 4 * io_bytes) + 2 * batch * N * io_bytes + D * (N + 2) * 4
+
+
+def bench_decode(args):
+    """Chained single-token decode steps against the cached fp32 state (256 x 5120 x 16).
+
+    Eight pre-generated tokens are cycled so inputs stay resident in HBM.  The
+    84 MB state is read and written every step; between steps it may stay in
+    the 256 MB Infinity Cache, as it would in a serving loop.  This path is
+    HBM-bound: the roofline is bytes against 8 TB/s.
+    """
+    import torch
+    from selective_state_space_39_amd import binding, inputs
+    batch, D = 256, 5120
+    dev = torch.device("cuda:0")
+    A, Dskip, dt_bias, h0 = inputs.decode_params(batch, D)
+    f32 = lambda a: torch.from_numpy(a).to(dev)
+    bf = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    toks = [inputs.decode_token(i, batch, D) for i in range(8)]
+    dtoks = [tuple(bf(getattr(t, n)) for n in ("x", "delta", "z", "B", "C")) for t in toks]
+    tA, tD, tb = f32(A), f32(Dskip), f32(dt_bias)
+    h = f32(h0)
+    y = torch.empty((batch, D), dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def step():
+        x, dl, z, B, C = dtoks[it[0] & 7]
+        it[0] += 1
+        binding.state_update(h, x, dl, tA, B, C, tD, tb, z=z, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms_per_step = timed(args.steps) / args.steps
+    binding.timing_collect()
+    binding.timing_enable(True, "s6_step")
+    timed(args.steps)
+    binding.timing_enable(False)
+    c, kms = binding.timing_collect()["s6_step"]
+    avg_ms = kms / c
+    abytes = decode_bytes(batch, D)
+    achieved = abytes / (avg_ms * 1e-3) / 1e9
+    out = {"metric": METRIC, "value": round(batch * D / (ms_per_step * 1e-3), 1), "unit": "elements/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "decode-256x5120 ssm_state_update", "batch": batch, "D": D, "N": 16,
+                      "io": "bf16", "state": "f32", "gated": True},
+           "hbm": {"achieved_gbps": round(abytes / (ms_per_step * 1e-3) / 1e9, 1), "peak_gbps": PEAK_HBM_GBPS,
+                   "frac": round(abytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                   "algorithmic_bytes_per_step": abytes},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                        "traffic": measured_traffic(args.workload, "s6_step"), "kernel": "s6_step",
+                        "avg_launch_ms": round(avg_ms, 5),
+                        "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters)"}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,7 +227,17 @@ def main():
     ap.add_argument("--workload", default="mamba-130m-layer", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (profile it for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files into profiles/traffic.json")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the scan shards over batch rows and channels with no communication, so N GPUs "
@@ -120,6 +251,8 @@ def main():
         sys.exit(1)
 
     k = WORKLOADS[args.workload]
+    if k == 5:
+        return bench_decode(args)
     s = inputs.make_config(k)
     batch, L, D, N = s.shape
     io = s.io
