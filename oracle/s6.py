@@ -33,11 +33,21 @@ What it computes, for every batch row b, channel d and state index n
 
 B and C are (batch, L, N) and shared by all channels of a batch row.
 
+Backward.  scan_bwd returns the gradient of J = sum(dout * out) +
+sum(dh_last * h_L) with respect to every input: the chain rule of the
+recurrence above, run backward in time over the stored float64 states.
+Training differentiates through the scan and the pages' own kernel recomputes
+the states for it instead of storing them ("DL0170 ...", point (3) and the
+paragraph after Figure 1); here they are simply stored.
+
 Parity status: pinned.  The test suite checks this module against the
 Delta -> 0 pass-through, the LTI convolution (direct sum, FFT and geometric
 closed form), a brute-force causal-matrix sum ("Mamba", "Relation to
 Mamba-2"), the overwrite limit ("DL0170 ...", point (2)), pure decay in
-closed form, sequence splitting and chained decode steps, and linearity.
+closed form, sequence splitting and chained decode steps, and linearity; the
+backward against central finite differences of that brute-force sum, exact
+dot-product identities of the inputs in which the output is linear, the LTI
+transposed convolution, a one-token closed form and gradient splitting.
 """
 from __future__ import annotations
 
@@ -144,3 +154,83 @@ def state_update(h, x, delta, A, B, C, Dskip, dt_bias, z=None, io: str = "f64"):
     zz = None if z is None else np.asarray(z, dtype=np.float64)[:, None, :]
     y, hn = scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=zz, h0=h)
     return y[:, 0, :], hn
+
+
+# ---------------------------------------------------------------------------
+# the backward pass
+# ---------------------------------------------------------------------------
+
+def _sigmoid(v):
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-v))
+
+
+def scan_bwd(x, delta, A, B, C, Dskip, dt_bias, dout, z=None, h0=None, dh_last=None, io: str = "f64"):
+    """Gradients of J = sum(dout * out) + sum(dh_last * h_L) for scan_fwd.
+
+    Same inputs as scan_fwd, plus dout (bt, L, D) (stored like x) and dh_last
+    (bt, D, N) or None (zero; always numbers, not io storage).  Returns a dict
+    of float64 arrays keyed by input name: x, delta, z (None when ungated), A,
+    B, C, Dskip, dt_bias, h0 (the gradient with respect to the starting state,
+    also when h0 itself is None, i.e. zeros).
+
+    Forward (stored): Delta_t = softplus(v_t), v_t = delta_t + dt_bias;
+    Abar_t = exp(Delta_t A); h_t = Abar_t h_{t-1} + Delta_t x_t B_t;
+    y_t = C_t . h_t + Dskip x_t; out_t = y_t silu(z_t).
+    Backward: dy_t = dout_t silu(z_t); mu_t = dJ/dh_t obeys
+    mu_t = C_t dy_t + Abar_{t+1} mu_{t+1}, with mu_{L-1} also receiving
+    dh_last; every other gradient is a product of mu_t with the forward
+    quantities of the same token.
+    """
+    if io != "f64":
+        x, delta, B, C, dout = (decode(a, io) for a in (x, delta, B, C, dout))
+        z = None if z is None else decode(z, io)
+    x = np.asarray(x, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    Dskip = np.asarray(Dskip, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    bt, L, D = x.shape
+    N = A.shape[1]
+    v = np.asarray(delta, dtype=np.float64) + np.asarray(dt_bias, dtype=np.float64)[None, None, :]
+    Delta = softplus(v)
+
+    # forward, keeping every state: hs[:, t + 1] = h_t, hs[:, 0] = h0
+    hs = np.empty((bt, L + 1, D, N))
+    hs[:, 0] = 0.0 if h0 is None else np.asarray(h0, dtype=np.float64)
+    for t in range(L):
+        Abar = np.exp(Delta[:, t, :, None] * A[None, :, :])
+        hs[:, t + 1] = Abar * hs[:, t] + (Delta[:, t, :] * x[:, t, :])[:, :, None] * B[:, t, None, :]
+    y = np.einsum("btdn,btn->btd", hs[:, 1:], C) + Dskip[None, None, :] * x
+
+    if z is not None:
+        z = np.asarray(z, dtype=np.float64)
+        sg = _sigmoid(z)
+        dy = dout * z * sg
+        dz = dout * y * sg * (1.0 + z * (1.0 - sg))   # d silu / dz = sigmoid (1 + z (1 - sigmoid))
+    else:
+        dy = dout
+        dz = None
+
+    dx = np.empty((bt, L, D))
+    dDelta = np.empty((bt, L, D))
+    dB = np.empty((bt, L, N))
+    dC = np.einsum("btd,btdn->btn", dy, hs[:, 1:])
+    dA = np.zeros((D, N))
+    # carried adjoint: the part of mu_t that comes from later tokens (and dh_last)
+    carry = np.zeros((bt, D, N)) if dh_last is None else np.array(dh_last, dtype=np.float64)
+    for t in range(L - 1, -1, -1):
+        mu = dy[:, t, :, None] * C[:, t, None, :] + carry                 # (bt, D, N)
+        Abar = np.exp(Delta[:, t, :, None] * A[None, :, :])
+        w = mu * Abar * hs[:, t]                                          # dJ/d(Delta_t A) per state
+        du = np.einsum("bdn,bn->bd", mu, B[:, t])                         # dJ/d(Delta_t x_t)
+        dx[:, t] = du * Delta[:, t] + dy[:, t] * Dskip[None, :]
+        dDelta[:, t] = du * x[:, t] + np.einsum("bdn,dn->bd", w, A)
+        dB[:, t] = np.einsum("bdn,bd->bn", mu, Delta[:, t] * x[:, t])
+        dA += np.einsum("bdn,bd->dn", w, Delta[:, t])
+        carry = Abar * mu
+    dv = dDelta * _sigmoid(v)                                             # softplus' = sigmoid
+    return dict(x=dx, delta=dv, z=dz, A=dA, B=dB, C=dC,
+                Dskip=np.einsum("btd,btd->d", dy, x), dt_bias=dv.sum(axis=(0, 1)), h0=carry)

@@ -1,7 +1,7 @@
 """Pins for the float64 oracle: results the pages and the mathematics fix.
 
 Each pin takes an oracle module ``m`` (exposing softplus, silu, recurrence,
-scan_fwd and state_update) and raises AssertionError when ``m`` disagrees
+scan_fwd, state_update and scan_bwd) and raises AssertionError when ``m`` disagrees
 with a value that does not come from ``m`` itself. The same pins run against
 copies of the oracle with a planted mistake (tests/test_oracle_mutants.py),
 which must each fail at least one of them.
@@ -375,6 +375,147 @@ def pin_linearity(m):
     _close(h3, al * h1 + be * h2, 1e-12, "linearity h")
 
 
+# ---------------------------------------------------------------------------
+# (h) the backward pass
+# ---------------------------------------------------------------------------
+
+_GRAD_INPUTS = ("x", "delta", "z", "A", "B", "C", "Dskip", "dt_bias", "h0")
+
+
+def _bf_objective(p, dout, dh_last):
+    """J = sum(dout * out) + sum(dh_last * h_L), through the brute-force sum.
+
+    Written independently of the oracle: its own softplus, its own gate and
+    the explicit causal-matrix form above.
+    """
+    Delta = _sp(p["delta"] + p["dt_bias"][None, None, :])
+    y, hL = brute_force(Delta, p["x"], p["A"], p["B"], p["C"], p["Dskip"], p["h0"])
+    if p.get("z") is not None:
+        y = y * (p["z"] / (1.0 + np.exp(-p["z"])))
+    J = float(np.sum(dout * y))
+    if dh_last is not None:
+        J += float(np.sum(dh_last * hL))
+    return J
+
+
+def _bwd_case(seed, bt, L, D, N, gated=True, with_h0=True, with_dh=True):
+    r = _rng(seed)
+    A, Dskip, dt_bias = _params(r, D, N, "rand")
+    p = dict(x=r.standard_normal((bt, L, D)), delta=r.standard_normal((bt, L, D)),
+             z=r.standard_normal((bt, L, D)) if gated else None,
+             B=r.standard_normal((bt, L, N)), C=r.standard_normal((bt, L, N)),
+             A=A, Dskip=Dskip, dt_bias=dt_bias + 1.5,   # steps near 0.1-1: decay and input both matter
+             h0=r.standard_normal((bt, D, N)) if with_h0 else None)
+    dout = r.standard_normal((bt, L, D))
+    dh = r.standard_normal((bt, D, N)) if with_dh else None
+    return p, dout, dh
+
+
+def _oracle_bwd(m, p, dout, dh):
+    return m.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["Dskip"], p["dt_bias"], dout,
+                      z=p["z"], h0=p["h0"], dh_last=dh)
+
+
+def pin_bwd_finite_differences(m):
+    """Every gradient equals central finite differences of the brute-force objective.
+
+    Steps of 1e-6 in float64 leave a truncation error near 1e-12 and a rounding
+    error near 1e-10 of the objective's size, far inside the 1e-6 bound.
+    """
+    for seed, shape, gated, with_h0, with_dh in [(20, (2, 6, 2, 3), True, True, True),
+                                                 (21, (1, 5, 3, 4), False, False, False)]:
+        p, dout, dh = _bwd_case(seed, *shape, gated=gated, with_h0=with_h0, with_dh=with_dh)
+        g = _oracle_bwd(m, p, dout, dh)
+        if not gated:
+            assert g["z"] is None, "ungated scan has no gate gradient"
+        for name in _GRAD_INPUTS:
+            if p.get(name) is None:
+                if name == "h0":       # gradient at h0 = 0
+                    base = dict(p, h0=np.zeros((shape[0], shape[2], shape[3])))
+                else:
+                    continue
+            else:
+                base = p
+            fd = np.zeros_like(base[name])
+            for idx in np.ndindex(*base[name].shape):
+                eps = 1e-6 * max(1.0, abs(base[name][idx]))
+                hi = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in base.items()}
+                lo = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in base.items()}
+                hi[name][idx] += eps
+                lo[name][idx] -= eps
+                fd[idx] = (_bf_objective(hi, dout, dh) - _bf_objective(lo, dout, dh)) / (2 * eps)
+            _close(g[name], fd, 1e-6, f"finite differences d{name} (case {seed})")
+
+
+def pin_bwd_dot_products(m):
+    """Exact identities where J is affine in an input: J(X) - J(X = 0) = <dJ/dX, X>.
+
+    With the other inputs fixed, out and h_L are linear in x (with h0 = 0), in
+    B, in C, in Dskip and in h0 (with x = 0), so the identity holds up to
+    rounding, at a length no finite difference would reach as precisely.
+    """
+    p, dout, dh = _bwd_case(22, 2, 24, 3, 16)
+    zero = lambda **kw: dict(p, **kw)
+    xz = np.zeros_like(p["x"])
+    cases = [("x", zero(h0=None), zero(h0=None, x=xz)),
+             ("B", p, zero(B=np.zeros_like(p["B"]))),
+             ("C", p, zero(C=np.zeros_like(p["C"]))),
+             ("Dskip", p, zero(Dskip=np.zeros_like(p["Dskip"]))),
+             ("h0", zero(x=xz), zero(x=xz, h0=np.zeros_like(p["h0"])))]
+    for name, at, at0 in cases:
+        g = _oracle_bwd(m, at, dout, dh)
+        lhs = _bf_objective(at, dout, dh) - _bf_objective(at0, dout, dh)
+        rhs = float(np.sum(g[name] * at[name]))
+        assert abs(lhs - rhs) <= 1e-11 * max(abs(lhs), 1.0), f"dot product d{name}: {lhs!r} vs {rhs!r}"
+
+
+def pin_bwd_lti_transpose(m):
+    """Constant step, B and C, ungated: y = K * x + D x is a causal convolution, so
+    dJ/dx is the correlation of dout with K plus D dout, and dJ/dh0_n is
+    sum_t dout_t C_n exp((t + 1) Delta A_n) (the S4 convolution view the pages
+    contrast Mamba with: "DL0170 ...", point (3))."""
+    r = _rng(23)
+    bt, L, D, N = 1, 64, 2, 16
+    A, Dskip, dt_bias = _params(r, D, N, "rand")
+    Bv = r.standard_normal(N)
+    Cv = r.standard_normal(N)
+    x = r.standard_normal((bt, L, D))
+    h0 = r.standard_normal((bt, D, N))
+    dout = r.standard_normal((bt, L, D))
+    g = m.scan_bwd(x, np.zeros((bt, L, D)), A, np.tile(Bv, (bt, L, 1)), np.tile(Cv, (bt, L, 1)),
+                   Dskip, dt_bias, dout, h0=h0)
+    Delta = _sp(dt_bias)
+    k = np.arange(L, dtype=np.float64)
+    for d in range(D):
+        decay = np.exp(np.outer(k, Delta[d] * A[d]))                     # (L, N): exp(k Delta A)
+        K = decay @ (Cv * Delta[d] * Bv)
+        go = dout[0, :, d]
+        ref = np.convolve(go[::-1], K)[:L][::-1] + Dskip[d] * go
+        _close(g["x"][0, :, d], ref, 1e-12, f"LTI transposed convolution, channel {d}")
+        ref_h0 = (decay * np.exp(Delta[d] * A[d])[None, :]).T @ go * Cv
+        _close(g["h0"][0, d], ref_h0, 1e-12, f"LTI dh0, channel {d}")
+
+
+def pin_bwd_split(m):
+    """Backward of scan(0:L) = backward of scan(L1:L) then of scan(0:L1), the
+    second receiving the first's starting-state gradient as its dh_last."""
+    p, dout, dh = _bwd_case(24, 2, 30, 3, 16)
+    whole = _oracle_bwd(m, p, dout, dh)
+    for L1 in (1, 13, 29):
+        a = {k: (v[:, :L1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in p.items()}
+        b = {k: (v[:, L1:] if k in ("x", "delta", "z", "B", "C") else v) for k, v in p.items()}
+        _, hmid = m.scan_fwd(a["x"], a["delta"], p["A"], a["B"], a["C"], p["Dskip"], p["dt_bias"], h0=p["h0"])
+        b["h0"] = hmid
+        gb = _oracle_bwd(m, b, dout[:, L1:], dh)
+        ga = _oracle_bwd(m, a, dout[:, :L1], gb["h0"])
+        for k in ("x", "delta", "z", "B", "C"):
+            _close(np.concatenate([ga[k], gb[k]], axis=1), whole[k], 1e-12, f"split {L1} d{k}")
+        for k in ("A", "Dskip", "dt_bias"):
+            _close(ga[k] + gb[k], whole[k], 1e-12, f"split {L1} d{k}")
+        _close(ga["h0"], whole["h0"], 1e-12, f"split {L1} dh0")
+
+
 PINS = [pin_softplus, pin_silu, pin_delta_zero_exact, pin_delta_tiny_bias, pin_lti_direct,
         pin_lti_fft, pin_lti_closed_form, pin_lti_lfilter, pin_brute_force, pin_overwrite,
-        pin_pure_decay, pin_single_token, pin_split, pin_chained_steps, pin_linearity]
+        pin_pure_decay, pin_single_token, pin_split, pin_chained_steps, pin_linearity,
+        pin_bwd_finite_differences, pin_bwd_dot_products, pin_bwd_lti_transpose, pin_bwd_split]

@@ -47,6 +47,33 @@ MUTANTS = {
                              "y, hn = scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=None, h0=h)"),
     "gate-before-skip": ("    if z is not None:\n        y = y * silu(z)\n",
                          "    if z is not None:\n        y = (y - Dskip * x) * silu(z) + Dskip * x\n"),
+    # the backward pass
+    "bwd-carry-not-decayed": ("        carry = Abar * mu\n", "        carry = mu\n"),
+    "bwd-decay-term-uses-new-state": ("w = mu * Abar * hs[:, t]", "w = mu * Abar * hs[:, t + 1]"),
+    "bwd-dx-skip-dropped": ("dx[:, t] = du * Delta[:, t] + dy[:, t] * Dskip[None, :]", "dx[:, t] = du * Delta[:, t]"),
+    "bwd-dx-skip-uses-dout": ("dx[:, t] = du * Delta[:, t] + dy[:, t] * Dskip[None, :]",
+                              "dx[:, t] = du * Delta[:, t] + dout[:, t] * Dskip[None, :]"),
+    "bwd-ddelta-input-term-dropped": ("dDelta[:, t] = du * x[:, t] + ", "dDelta[:, t] = "),
+    "bwd-ddelta-decay-term-dropped": ("dDelta[:, t] = du * x[:, t] + np.einsum(\"bdn,dn->bd\", w, A)",
+                                      "dDelta[:, t] = du * x[:, t]"),
+    "bwd-softplus-derivative-dropped": ("dv = dDelta * _sigmoid(v)", "dv = dDelta"),
+    "bwd-dz-silu-derivative-truncated": ("dz = dout * y * sg * (1.0 + z * (1.0 - sg))", "dz = dout * y * sg"),
+    "bwd-dy-ignores-gate": ("dy = dout * z * sg", "dy = dout"),
+    "bwd-dC-previous-state": ("dC = np.einsum(\"btd,btdn->btn\", dy, hs[:, 1:])",
+                              "dC = np.einsum(\"btd,btdn->btn\", dy, hs[:, :-1])"),
+    "bwd-dB-without-delta": ("np.einsum(\"bdn,bd->bn\", mu, Delta[:, t] * x[:, t])",
+                             "np.einsum(\"bdn,bd->bn\", mu, x[:, t])"),
+    "bwd-dA-without-delta": ("dA += np.einsum(\"bdn,bd->dn\", w, Delta[:, t])",
+                             "dA += np.einsum(\"bdn,bd->dn\", w, np.ones_like(Delta[:, t]))"),
+    "bwd-dh-last-ignored": ("carry = np.zeros((bt, D, N)) if dh_last is None else np.array(dh_last, dtype=np.float64)",
+                            "carry = np.zeros((bt, D, N))"),
+    "bwd-dh0-undecayed": ("dt_bias=dv.sum(axis=(0, 1)), h0=carry)", "dt_bias=dv.sum(axis=(0, 1)), h0=mu)"),
+    "bwd-adjoint-reads-B": ("mu = dy[:, t, :, None] * C[:, t, None, :] + carry",
+                            "mu = dy[:, t, :, None] * B[:, t, None, :] + carry"),
+    "bwd-du-reads-C": ("du = np.einsum(\"bdn,bn->bd\", mu, B[:, t])", "du = np.einsum(\"bdn,bn->bd\", mu, C[:, t])"),
+    "bwd-dDskip-uses-dout": ("Dskip=np.einsum(\"btd,btd->d\", dy, x)", "Dskip=np.einsum(\"btd,btd->d\", dout, x)"),
+    "bwd-dbias-before-softplus-derivative": ("dt_bias=dv.sum(axis=(0, 1))", "dt_bias=dDelta.sum(axis=(0, 1))"),
+    "bwd-dz-ungated-output": ("dz = dout * y * sg", "dz = dout * (y - Dskip * x) * sg"),
 }
 
 
