@@ -147,6 +147,62 @@ int ssm_state_update(float* h,
                      void* stream);
 
 /*
+ * Workspace bytes and chunk plan of ssm_scan_bwd for this shape (the
+ * backward always needs a workspace).  chunk_len as for ssm_scan_bwd.
+ * Host-only; negative ssm_status for an invalid shape.
+ */
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                     int io_dtype, int64_t chunk_len);
+int ssm_scan_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                      int64_t chunk_len, int64_t* chunk_len_out, int64_t* n_chunks_out);
+
+/*
+ * Backward of ssm_scan_fwd: gradients of J = sum(dout * out) + sum(dh_last * h_L)
+ * with respect to every input.
+ *
+ * Training differentiates through the scan, and the pages' kernel recomputes
+ * the states for it rather than storing them ("DL0170 Mamba Selective SSM vs
+ * Attention", point (3) and the paragraph after Figure 1).  So does this
+ * call: it takes the forward's inputs, not its activations.  The adjoint
+ * mu_t = dJ/dh_t runs backward in time, mu_t = C_t dy_t + Abar_{t+1} mu_{t+1}
+ * with dy_t = dout_t * silu(z_t), and is chunked with the same carry algebra
+ * as the forward state; within a chunk the states are recomputed a few tokens
+ * at a time from stored sub-chunk starting states.
+ *
+ *   x, delta, z, B, C, A, Dskip, dt_bias, h0   as passed to ssm_scan_fwd
+ *                   (z NULL = ungated, h0 NULL = zero initial state).
+ *   dout            (batch, L, D) io dtype, required.
+ *   dh_last         (batch, D, N) float32 gradient of h_L; NULL = zero.
+ *   dx, ddelta      (batch, L, D) io dtype outputs, required.
+ *   dz              (batch, L, D) io dtype output; required when z is given,
+ *                   NULL when z is NULL.
+ *   dB, dC          (batch, L, N) float32 outputs (summed over channels).
+ *   dA              (D, N) float32 output; dDskip, ddt_bias (D) float32
+ *                   outputs (summed over batch rows and tokens).  Outputs are
+ *                   overwritten, not accumulated into.
+ *   dh0             (batch, D, N) float32 output or NULL (not wanted); the
+ *                   gradient with respect to the starting state, also when
+ *                   h0 is NULL.
+ *   chunk_len       0 = the library's plan; else a positive multiple of 32.
+ *   workspace       at least ssm_scan_bwd_workspace_bytes(...) bytes,
+ *                   256-byte aligned, required.
+ * Alignment as for ssm_scan_fwd (dout, dx, ddelta, dz like x).  No output may
+ * overlap an input, another output or the workspace.  The sums over channels,
+ * tokens and batch rows are taken in a fixed order: results are bitwise
+ * reproducible for a given shape and chunk_len.
+ */
+int ssm_scan_bwd(const void* x, const void* delta, const void* z,
+                 const void* B, const void* C,
+                 const float* A, const float* Dskip, const float* dt_bias,
+                 const float* h0,
+                 const void* dout, const float* dh_last,
+                 void* dx, void* ddelta, void* dz, float* dB, float* dC,
+                 float* dA, float* dDskip, float* ddt_bias, float* dh0,
+                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                 int64_t chunk_len, void* workspace, int64_t workspace_bytes,
+                 void* stream);
+
+/*
  * Per-kernel timing, for measurement tools; not needed to compute anything.
  *
  * ssm_timing_enable(1, kernel) makes every later launch of the named kernel
@@ -154,8 +210,9 @@ int ssm_state_update(float* h,
  * bracketed by two hipEvents recorded on the launch's own stream;
  * ssm_timing_enable(0, NULL) stops recording.  Recording events between
  * kernels costs time, so time whole calls with recording off.  Kernel names:
- * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step".  Returns
- * SSM_OK.
+ * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step", and for the
+ * backward "s6_chunk_carry_rev", "s6_carry_scan_rev", "s6_chunk_bwd",
+ * "s6_reduce_bc", "s6_reduce_params".  Returns SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the

@@ -47,6 +47,12 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_plan.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ssm_scan_fwd.restype = i32
     L.ssm_scan_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
+    L.ssm_scan_bwd_workspace_bytes.restype = i64
+    L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
+    L.ssm_scan_bwd_plan.restype = i32
+    L.ssm_scan_bwd_plan.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.ssm_scan_bwd.restype = i32
+    L.ssm_scan_bwd.argtypes = [vp] * 20 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_state_update.restype = i32
     L.ssm_state_update.argtypes = [vp] * 10 + [i64, i64, i64, i32, vp]
     L.ssm_timing_enable.restype = i32
@@ -150,6 +156,78 @@ def scan_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, chunk_len: int = 0,
                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc)
     return y, h_last
+
+
+def bwd_workspace_bytes(batch: int, L: int, D: int, io_dtype: int = SSM_BF16, chunk_len: int = 0) -> int:
+    n = lib().ssm_scan_bwd_workspace_bytes(batch, L, D, N_STATE, io_dtype, chunk_len)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def bwd_plan(batch: int, L: int, D: int, io_dtype: int = SSM_BF16, chunk_len: int = 0) -> Tuple[int, int]:
+    """(chunk length, number of chunks) of the backward for this shape."""
+    cl, nc = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ssm_scan_bwd_plan(batch, L, D, N_STATE, io_dtype, chunk_len, ctypes.byref(cl), ctypes.byref(nc)))
+    return cl.value, nc.value
+
+
+BWD_OUTPUTS = ("x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0")
+
+
+def scan_bwd(x, delta, A, B, C, D, dt_bias, dout, z=None, h0=None, dh_last=None, chunk_len: int = 0,
+             want_dh0: bool = True, workspace=None, grads=None):
+    """Gradients of sum(dout * out) + sum(dh_last * h_last) for scan_fwd with the same inputs.
+
+    Returns a dict keyed by input name: "x", "delta", "z" (io dtype, "z" None
+    when ungated), "B", "C" (batch, L, 16), "A" (D, 16), "Dskip", "dt_bias"
+    (D,), all float32, and "h0" (batch, D, 16) float32 (None unless want_dh0).
+    `grads` may hold preallocated outputs under the same keys.
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, D)")
+    batch, L, Dc = x.shape
+    dev = x.device
+    io = _io(x)
+    dt = x.dtype
+    for t, name in ((x, "x"), (delta, "delta"), (dout, "dout")):
+        _need(t, name, (batch, L, Dc), dt, dev)
+    if z is not None:
+        _need(z, "z", (batch, L, Dc), dt, dev)
+    _need(B, "B", (batch, L, N_STATE), dt, dev)
+    _need(C, "C", (batch, L, N_STATE), dt, dev)
+    _need(A, "A", (Dc, N_STATE), torch.float32, dev)
+    _need(D, "D", (Dc,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (Dc,), torch.float32, dev)
+    for t, name in ((h0, "h0"), (dh_last, "dh_last")):
+        if t is not None:
+            _need(t, name, (batch, Dc, N_STATE), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(grads or {})
+    shapes = {"x": ((batch, L, Dc), dt), "delta": ((batch, L, Dc), dt), "z": ((batch, L, Dc), dt),
+              "B": ((batch, L, N_STATE), torch.float32), "C": ((batch, L, N_STATE), torch.float32),
+              "A": ((Dc, N_STATE), torch.float32), "Dskip": ((Dc,), torch.float32),
+              "dt_bias": ((Dc,), torch.float32), "h0": ((batch, Dc, N_STATE), torch.float32)}
+    for k, (shape, dty) in shapes.items():
+        if (k == "z" and z is None) or (k == "h0" and not want_dh0):
+            g[k] = None
+            continue
+        if g.get(k) is None:
+            g[k] = torch.empty(shape, dtype=dty, device=dev)
+        _need(g[k], "grad " + k, shape, dty, dev)
+    nws = bwd_workspace_bytes(batch, L, Dc, io, chunk_len)
+    if workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nws:
+        raise ValueError(f"workspace too small: {nws} bytes needed")
+    rc = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
+                            _ptr(h0), _ptr(dout), _ptr(dh_last),
+                            _ptr(g["x"]), _ptr(g["delta"]), _ptr(g["z"]), _ptr(g["B"]), _ptr(g["C"]),
+                            _ptr(g["A"]), _ptr(g["Dskip"]), _ptr(g["dt_bias"]), _ptr(g["h0"]),
+                            batch, L, Dc, N_STATE, io, chunk_len,
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return {k: g[k] for k in BWD_OUTPUTS}
 
 
 def state_update(h, x, delta, A, B, C, D, dt_bias, z=None, out=None):

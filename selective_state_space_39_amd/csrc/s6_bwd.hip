@@ -1,0 +1,488 @@
+// gfx950 kernels of the selective scan (S6) backward pass.
+//
+// The pages' kernel keeps the expanded states on chip and recomputes them for
+// the backward pass instead of storing the (batch, L, D, N) tensor ("DL0170
+// Mamba Selective SSM vs Attention", point (3) and the paragraph after
+// Figure 1).  Here, with the forward's layout (one lane per channel, its 16
+// states in VGPRs, B_t / C_t as SGPR operands):
+//
+//   dy_t   = dout_t * silu(z_t)                     (dout_t when ungated)
+//   mu_t   = dJ/dh_t = C_t dy_t + Abar_{t+1} mu_{t+1}, mu_{L-1} also gets dh_last
+//   w_tn   = mu_tn Abar_tn h_{t-1,n}                (dJ/d(Delta_t A_n))
+//   dx_t   = Delta_t sum_n mu_tn B_tn + Dskip dy_t
+//   dDelta = x_t sum_n mu_tn B_tn + sum_n w_tn A_n,  ddelta_t = dDelta sigmoid(v_t)
+//   dA_n  += w_tn Delta_t,   dB_tn += mu_tn Delta_t x_t,   dC_tn += dy_t h_tn
+//
+// The adjoint mu runs backward in time and has the same chunk algebra as the
+// state: a chunk scanned backward from mu = 0 leaves (S = sum Delta,
+// Lambda = Abar_{t0} mu_{t0}), and the incoming adjoint of chunk c-1 is
+// Lambda_c + exp(A S_c) * (incoming adjoint of chunk c).  Launch order:
+//   1. s6_chunk_carry + s6_carry_scan (the forward's): starting state per chunk;
+//   2. s6_chunk_carry_rev: adjoint carries of chunks 1..n-1;
+//      s6_carry_scan in reverse from dh_last: incoming adjoint per chunk;
+//   3. s6_chunk_bwd: per chunk, a forward sweep from the starting state stores
+//      the state at every kBwdSub-token sub-chunk start; then, sub-chunk by
+//      sub-chunk from the end, the states of the sub-chunk are recomputed into
+//      registers and the adjoint runs back through them;
+//   4. s6_reduce_bc / s6_reduce_params: deterministic sums of the per-wavefront
+//      dB, dC and per-chunk dA, dDskip, ddt_bias partials.
+
+#include "s6_device.h"
+
+namespace s6 {
+
+// x, delta, dout and z of kBlk tokens in reverse order: block k holds the
+// tokens first - j rows (j = 0..kBlk-1); rows before the chunk start are
+// clamped to row 0 and masked by the caller.
+template <class LD, int NT>
+struct StageRev {
+    using IO = typename LD::IO;
+    typename LD::R r[NT][kBlk];
+    float v[NT][kBlk];
+
+    __device__ __forceinline__ void issue(const LD& ld, const ChunkIO<IO> (&src)[NT], uint32_t vo, int first_row,
+                                          uint32_t rowb) {
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const int row = first_row - j;
+            const uint32_t o = static_cast<uint32_t>(row > 0 ? row : 0) * rowb;
+#pragma unroll
+            for (int k = 0; k < NT; ++k) r[k][j] = ld.load(src[k], vo, o);
+        }
+    }
+    __device__ __forceinline__ void widen(const LD& ld) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) v[k][j] = ld.widen(r[k][j]);
+    }
+};
+
+__device__ __forceinline__ float gate_grad(float g, float z, float& dz_per_y) {
+    // dy = g silu(z); dJ/dz = g y sigmoid(z) (1 + z (1 - sigmoid(z))), returned per unit y
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+    dz_per_y = g * sg * fmaf(z, 1.0f - sg, 1.0f);
+    return g * z * sg;
+}
+
+// ---------------------------------------------------------------------------
+// adjoint carries of chunks 1..n-1
+// ---------------------------------------------------------------------------
+template <class LD, bool GATED>
+__global__ __launch_bounds__(kBlock) void s6_chunk_carry_rev(S6BwdArgs a) {
+    using IO = typename LD::IO;
+    using T = typename IO::T;
+    constexpr int NT = GATED ? 3 : 2;          // delta, dout, z
+    LD ld;
+    constexpr uint32_t es = sizeof(T);
+    Geo g;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks - 1, 1, g)) return;
+    const uint32_t rowb = static_cast<uint32_t>(a.D) * es;
+    const uint32_t bytes = static_cast<uint32_t>(g.nt) * rowb;
+    const int64_t e0 = g.row0 * a.D;
+    ChunkIO<IO> src[NT];
+    src[0].init(static_cast<const T*>(a.delta) + e0, bytes);
+    src[1].init(static_cast<const T*>(a.dout) + e0, bytes);
+    if (GATED) src[2].init(static_cast<const T*>(a.z) + e0, bytes);
+    const T* Cc = static_cast<const T*>(a.C) + g.row0 * kN;
+    const uint32_t vo = ld.voff(g.d);
+
+    float A2[kN], rho[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { A2[n] = a.A[g.d * kN + n] * kLog2e; rho[n] = 0.0f; }
+    const float bias = a.dt_bias[g.d];
+    float S = 0.0f;
+
+    StageRev<LD, NT> st;
+    st.issue(ld, src, vo, g.nt - 1, rowb);
+    st.widen(ld);
+    RowBC<IO> cq[2];
+    cq[0].load(Cc + (g.nt - 1) * kN);
+    for (int tb = 0; tb < g.nt; tb += kBlk) {
+        st.issue(ld, src, vo, g.nt - 1 - tb - kBlk, rowb);
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const int tt = g.nt - 1 - (tb + j);
+            const bool valid = tt >= 0;                 // wave-uniform
+            lgkm_wait_all();
+            cq[(j + 1) & 1].load(Cc + max(tt - 1, 0) * kN);
+            const RowBC<IO>& Cv = cq[j & 1];
+            const float dt = valid ? softplus(st.v[0][j] + bias) : 0.0f;
+            float dy = st.v[1][j];
+            if (GATED) {
+                float unused;
+                dy = gate_grad(dy, st.v[2][j], unused);
+            }
+            dy = valid ? dy : 0.0f;
+            S += dt;
+#pragma unroll
+            for (int n = 0; n < kN; ++n) {
+                const float mu = fmaf(Cv.get(n), dy, rho[n]);
+                rho[n] = __builtin_amdgcn_exp2f(dt * A2[n]) * mu;
+            }
+        }
+        st.widen(ld);
+    }
+    const int64_t cs = static_cast<int64_t>(g.b) * (a.n_chunks - 1) + g.c - 1;
+    a.rcarry_S[cs * a.D + g.d] = S;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) a.rcarry_H[(cs * kN + n) * a.D + g.d] = rho[n];
+}
+
+// ---------------------------------------------------------------------------
+// sums of 16 per-lane values over the wavefront
+// ---------------------------------------------------------------------------
+// Reduce-scatter by halving: at each level a lane keeps one half of its
+// values, sends the other half to the lane that differs in one lane-index bit
+// and adds what it receives.  Afterwards lane l holds the wavefront sum of
+// value l >> 2 (the four lanes 4i..4i+3 hold the same sum).  Every value is
+// first scaled by `keep` (0 for lanes that only duplicate another channel).
+__device__ __forceinline__ float wave_sum16(float (&v)[16], float keep) {
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= keep;
+#pragma unroll
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int k = 32 >> lvl;          // lane distance 32, 16, 8, 4
+        const int half = 8 >> lvl;        // values kept after this level
+        // bit-select on the values (a select between two array elements could
+        // otherwise become a per-lane register index)
+        const uint32_t m = (lane & k) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + half]);
+            const float send = __uint_as_float((lo & m) | (hi & ~m));
+            const float kp = __uint_as_float((hi & m) | (lo & ~m));
+            v[i] = kp + __shfl_xor(send, k);
+        }
+    }
+    const float s = v[0] + __shfl_xor(v[0], 2);
+    return s + __shfl_xor(s, 1);
+}
+
+// A copy of a wave-uniform pointer that the compiler cannot prove equal to
+// the original, so scalar loads through it are not merged with earlier loads
+// of the same rows (which would keep those rows live in SGPRs in between).
+template <class P>
+__device__ __forceinline__ P* opaque(P* p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk backward
+// ---------------------------------------------------------------------------
+template <class LD, bool GATED>
+__global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
+    using IO = typename LD::IO;
+    using T = typename IO::T;
+    constexpr int SUB = kBwdSub;
+    static_assert(SUB % kBlk == 0 || kBlk % SUB == 0, "sub-chunks and load blocks must nest");
+    LD ld;
+    constexpr uint32_t es = sizeof(T);
+    Geo g;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks, 0, g)) return;
+    const int64_t D = a.D;
+    const uint32_t rowb = static_cast<uint32_t>(D) * es;
+    const uint32_t last = static_cast<uint32_t>(g.nt - 1) * rowb;
+    const int64_t e0 = g.row0 * D;
+    ChunkIO<IO> X, DL, GO, Z, DX, DDL, DZ;
+    X.init(static_cast<const T*>(a.x) + e0, last + rowb);
+    DL.init(static_cast<const T*>(a.delta) + e0, last + rowb);
+    GO.init(static_cast<const T*>(a.dout) + e0, last + rowb);
+    DX.init(static_cast<T*>(a.dx) + e0, last + rowb);
+    DDL.init(static_cast<T*>(a.ddelta) + e0, last + rowb);
+    if (GATED) {
+        Z.init(static_cast<const T*>(a.z) + e0, last + rowb);
+        DZ.init(static_cast<T*>(a.dz) + e0, last + rowb);
+    }
+    const T* Bc = static_cast<const T*>(a.B) + g.row0 * kN;
+    const T* Cc = static_cast<const T*>(a.C) + g.row0 * kN;
+    const uint32_t vo = ld.voff(g.d);
+    const uint32_t vs = g.d * es;
+    const int nsub = (g.nt + SUB - 1) / SUB;
+    const int64_t nsub_max = a.chunk_len / SUB;
+    float* ck = a.ckpt + ((static_cast<int64_t>(g.b) * a.n_chunks + g.c) * nsub_max * kN) * D + g.d;
+
+    float A2[kN], h[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) A2[n] = a.A[g.d * kN + n] * kLog2e;
+    const float bias = a.dt_bias[g.d];
+    const float Dd = a.Dskip[g.d];
+    const int64_t bd = static_cast<int64_t>(g.b) * D + g.d;
+    if (g.c > 0) {
+        const int64_t cs = static_cast<int64_t>(g.b) * (a.n_chunks - 1) + g.c - 1;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = a.carry_H[(cs * kN + n) * D + g.d];
+    } else if (a.h0) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = a.h0[bd * kN + n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+    }
+
+    // 1. forward sweep: the state at the start of every sub-chunk
+    {
+        const int sweep = (nsub - 1) * SUB;        // tokens before the last sub-chunk
+        const ChunkIO<IO> src[2] = {X, DL};
+        Stage<LD, 2> st;
+        st.issue(ld, src, vo, 0, rowb, last);
+        st.widen(ld);
+        RowBC<IO> bq[2];
+        bq[0].load(Bc);
+        for (int tb = 0; tb < sweep; tb += kBlk) {
+            st.issue(ld, src, vo, static_cast<uint32_t>(tb + kBlk) * rowb, rowb, last);
+#pragma unroll
+            for (int j = 0; j < kBlk; ++j) {
+                const int tt = tb + j;
+                if (tt % SUB == 0) {
+#pragma unroll
+                    for (int n = 0; n < kN; ++n) ck[(static_cast<int64_t>(tt / SUB) * kN + n) * D] = h[n];
+                }
+                lgkm_wait_all();
+                bq[(j + 1) & 1].load(Bc + min(tt + 1, g.nt - 1) * kN);
+                const RowBC<IO>& Bv = bq[j & 1];
+                const float dt = softplus(st.v[1][j] + bias);
+                const float dx = dt * st.v[0][j];
+#pragma unroll
+                for (int n = 0; n < kN; ++n)
+                    h[n] = fmaf(__builtin_amdgcn_exp2f(dt * A2[n]), h[n], dx * Bv.get(n));
+            }
+            st.widen(ld);
+        }
+    }
+
+    // 2. sub-chunks from the last to the first
+    float rho[kN], dA[kN];
+    if (g.c < a.n_chunks - 1) {
+        const int64_t cs = static_cast<int64_t>(g.b) * (a.n_chunks - 1) + g.c;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) rho[n] = a.rcarry_H[(cs * kN + n) * D + g.d];
+    } else if (a.dh_last) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) rho[n] = a.dh_last[bd * kN + n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) rho[n] = 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < kN; ++n) dA[n] = 0.0f;
+    float dD = 0.0f, dbias = 0.0f;
+    const int64_t G = (D + kWave - 1) / kWave;
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    float* pbc = a.part_bc + (g.row0 * G + g.group) * (2 * kN) + (lane >> 2);
+
+    for (int j = nsub - 1; j >= 0; --j) {
+        const int t0 = j * SUB;
+        if (j < nsub - 1) {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) h[n] = ck[(static_cast<int64_t>(j) * kN + n) * D];
+        }
+        // loads of the sub-chunk's tokens (rows past the chunk end clamp to its last row)
+        typename LD::R rx[SUB], rd[SUB], rg[SUB], rz[SUB];
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            const uint32_t o = min(static_cast<uint32_t>(t0 + i) * rowb, last);
+            rx[i] = ld.load(X, vo, o);
+            rd[i] = ld.load(DL, vo, o);
+            rg[i] = ld.load(GO, vo, o);
+            if (GATED) rz[i] = ld.load(Z, vo, o);
+        }
+        // recompute: states before each token, step sizes, dy (and dz)
+        float hs[SUB][kN];
+        float xs[SUB], dts[SUB], sgs[SUB], dys[SUB];
+        {
+            const T* Bs = opaque(Bc);
+            const T* Cs = opaque(Cc);
+            RowBC<IO> bq[2], cq[2];
+            lgkm_wait_all();
+            bq[0].load(Bs + min(t0, g.nt - 1) * kN);
+            if (GATED) cq[0].load(Cs + min(t0, g.nt - 1) * kN);
+#pragma unroll
+            for (int i = 0; i < SUB; ++i) {
+                const int tt = t0 + i;
+                const bool valid = tt < g.nt;                    // wave-uniform
+                lgkm_wait_all();
+                if (i + 1 < SUB) {
+                    bq[(i + 1) & 1].load(Bs + min(tt + 1, g.nt - 1) * kN);
+                    if (GATED) cq[(i + 1) & 1].load(Cs + min(tt + 1, g.nt - 1) * kN);
+                }
+                const RowBC<IO>& Bv = bq[i & 1];
+                const RowBC<IO>& Cv = cq[i & 1];
+#pragma unroll
+                for (int n = 0; n < kN; ++n) hs[i][n] = h[n];
+                const float xv = ld.widen(rx[i]);
+                float sg = 0.0f;
+                const float dt = valid ? softplus_sig(ld.widen(rd[i]) + bias, sg) : 0.0f;
+                const float u = dt * xv;
+                xs[i] = xv;
+                dts[i] = dt;
+                sgs[i] = sg;
+                float yv = Dd * xv;
+#pragma unroll
+                for (int n = 0; n < kN; ++n) {
+                    h[n] = fmaf(__builtin_amdgcn_exp2f(dt * A2[n]), h[n], u * Bv.get(n));
+                    if (GATED) yv = fmaf(Cv.get(n), h[n], yv);
+                }
+                float gv = ld.widen(rg[i]);
+                if (GATED) {
+                    float dzy;
+                    gv = gate_grad(gv, ld.widen(rz[i]), dzy);
+                    if (valid) store_io(DZ, vs, static_cast<uint32_t>(tt) * rowb, dzy * yv);
+                }
+                dys[i] = gv;
+            }
+        }
+        // adjoint back through the sub-chunk
+        {
+            const T* Bs = opaque(Bc);
+            const T* Cs = opaque(Cc);
+            RowBC<IO> bq[2], cq[2];
+            const int tl = min(t0 + SUB - 1, g.nt - 1);
+            lgkm_wait_all();
+            bq[(SUB - 1) & 1].load(Bs + tl * kN);
+            cq[(SUB - 1) & 1].load(Cs + tl * kN);
+#pragma unroll
+            for (int i = SUB - 1; i >= 0; --i) {
+                const int tt = t0 + i;
+                lgkm_wait_all();
+                if (i > 0) {
+                    bq[(i - 1) & 1].load(Bs + min(tt - 1, g.nt - 1) * kN);
+                    cq[(i - 1) & 1].load(Cs + min(tt - 1, g.nt - 1) * kN);
+                }
+                if (tt >= g.nt) continue;                         // wave-uniform
+                const RowBC<IO>& Bv = bq[i & 1];
+                const RowBC<IO>& Cv = cq[i & 1];
+                const float dy = dys[i];
+                float dt = dts[i];
+                asm volatile("" : "+v"(dt));     // recompute Abar here rather than keep 16 per token live
+                const float u = dt * xs[i];
+                float du = 0.0f, sw = 0.0f;
+                float pb[kN], pc[kN];
+#pragma unroll
+                for (int n = 0; n < kN; ++n) {
+                    const float ht = (i == SUB - 1) ? h[n] : hs[i + 1][n];
+                    const float mu = fmaf(Cv.get(n), dy, rho[n]);
+                    du = fmaf(mu, Bv.get(n), du);
+                    pc[n] = dy * ht;
+                    const float q = __builtin_amdgcn_exp2f(dt * A2[n]) * mu;
+                    const float w = q * hs[i][n];
+                    sw = fmaf(w, A2[n], sw);
+                    dA[n] = fmaf(w, dt, dA[n]);
+                    pb[n] = mu * u;
+                    rho[n] = q;
+                }
+                const float dxv = fmaf(du, dt, dy * Dd);
+                const float dv = fmaf(sw, kLn2, du * xs[i]) * sgs[i];
+                const uint32_t so = static_cast<uint32_t>(tt) * rowb;
+                store_io(DX, vs, so, dxv);
+                store_io(DDL, vs, so, dv);
+                dD = fmaf(dy, xs[i], dD);
+                dbias += dv;
+                const float keep = g.active ? 1.0f : 0.0f;      // duplicate lanes add nothing
+                const float sb = wave_sum16(pb, keep);
+                const float sc = wave_sum16(pc, keep);
+                if ((lane & 3) == 0) {
+                    float* q = pbc + static_cast<int64_t>(tt) * G * (2 * kN);
+                    q[0] = sb;
+                    q[kN] = sc;
+                }
+            }
+        }
+    }
+    if (g.c == 0 && a.dh0) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) a.dh0[bd * kN + n] = rho[n];
+    }
+    if (g.active) {
+        float* pp = a.part_p + (static_cast<int64_t>(g.b) * a.n_chunks + g.c) * kBwdParams * D + g.d;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) pp[n * D] = dA[n];
+        pp[kN * D] = dD;
+        pp[(kN + 1) * D] = dbias;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// deterministic reductions of the partial sums
+// ---------------------------------------------------------------------------
+// dB, dC: one lane per (b, t, k), k < 2N; sums the ceil(D / 64) wavefront partials.
+__global__ __launch_bounds__(kBlock) void s6_reduce_bc(S6BwdArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= a.batch * a.L * 2 * kN) return;
+    const int64_t row = i / (2 * kN);
+    const int k = static_cast<int>(i % (2 * kN));
+    const int64_t G = (a.D + kWave - 1) / kWave;
+    const float* p = a.part_bc + row * G * (2 * kN) + k;
+    float s = 0.0f;
+    for (int64_t gi = 0; gi < G; ++gi) s += p[gi * 2 * kN];
+    if (k < kN) a.dB[row * kN + k] = s;
+    else a.dC[row * kN + k - kN] = s;
+}
+
+// dA, dDskip, ddt_bias: one lane per (k, d); sums the batch x chunk partials.
+__global__ __launch_bounds__(kBlock) void s6_reduce_params(S6BwdArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= kBwdParams * a.D) return;
+    const int64_t k = i / a.D, d = i % a.D;
+    const int64_t units = a.batch * a.n_chunks;
+    const float* p = a.part_p + k * a.D + d;
+    float s = 0.0f;
+    for (int64_t u = 0; u < units; ++u) s += p[u * kBwdParams * a.D];
+    if (k < kN) a.dA[d * kN + k] = s;
+    else if (k == kN) a.dDskip[d] = s;
+    else a.ddt_bias[d] = s;
+}
+
+}  // namespace s6
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+using namespace s6;
+
+template <class LD, bool GATED>
+static hipError_t launch_bwd_t(const S6BwdArgs& a, hipStream_t stream) {
+    const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
+    if (a.n_chunks > 1) {
+        S6ScanArgs f{};
+        f.x = a.x; f.delta = a.delta; f.B = a.B; f.C = a.C;
+        f.A = a.A; f.Dskip = a.Dskip; f.dt_bias = a.dt_bias; f.h0 = a.h0;
+        f.carry_S = a.carry_S; f.carry_H = a.carry_H;
+        f.batch = a.batch; f.L = a.L; f.D = a.D; f.chunk_len = a.chunk_len; f.n_chunks = a.n_chunks;
+        f.bf16 = a.bf16; f.pair_loads = a.pair_loads;
+        s6_launch_chunk_carry(f, stream);
+        s6_launch_fold(S6FoldArgs{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0},
+                       "s6_carry_scan", stream);
+        dim3 g1(static_cast<unsigned>(nblk * (a.n_chunks - 1)));
+        s6_timing_mark("s6_chunk_carry_rev", stream, true);
+        hipLaunchKernelGGL((s6_chunk_carry_rev<LD, GATED>), g1, dim3(kBlock), 0, stream, a);
+        s6_timing_mark("s6_chunk_carry_rev", stream, false);
+        s6_launch_fold(S6FoldArgs{a.A, a.dh_last, a.rcarry_S, a.rcarry_H, a.batch, a.D, a.n_chunks - 1, 1},
+                       "s6_carry_scan_rev", stream);
+    }
+    dim3 g3(static_cast<unsigned>(nblk * a.n_chunks));
+    s6_timing_mark("s6_chunk_bwd", stream, true);
+    hipLaunchKernelGGL((s6_chunk_bwd<LD, GATED>), g3, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_chunk_bwd", stream, false);
+    const int64_t nbc = a.batch * a.L * 2 * kN;
+    s6_timing_mark("s6_reduce_bc", stream, true);
+    hipLaunchKernelGGL(s6_reduce_bc, dim3(static_cast<unsigned>((nbc + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       stream, a);
+    s6_timing_mark("s6_reduce_bc", stream, false);
+    const int64_t np = kBwdParams * a.D;
+    s6_timing_mark("s6_reduce_params", stream, true);
+    hipLaunchKernelGGL(s6_reduce_params, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       stream, a);
+    s6_timing_mark("s6_reduce_params", stream, false);
+    return hipGetLastError();
+}
+
+hipError_t s6_launch_bwd(const S6BwdArgs& a, hipStream_t stream) {
+    const bool gated = a.z != nullptr;
+    if (a.bf16 && a.pair_loads)
+        return gated ? launch_bwd_t<LdPairBF16, true>(a, stream) : launch_bwd_t<LdPairBF16, false>(a, stream);
+    if (a.bf16) return gated ? launch_bwd_t<LdBF16, true>(a, stream) : launch_bwd_t<LdBF16, false>(a, stream);
+    return gated ? launch_bwd_t<LdF32, true>(a, stream) : launch_bwd_t<LdF32, false>(a, stream);
+}

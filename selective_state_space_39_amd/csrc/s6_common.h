@@ -46,6 +46,17 @@ __device__ __forceinline__ float softplus(float v) {
     return fmaxf(v, 0.0f) + fmaf(__builtin_amdgcn_logf(u), kLn2, lost);
 }
 
+// softplus(v) and its derivative sigmoid(v), sharing exp(-|v|):
+// sigmoid(v) = 1 / (1 + e) for v >= 0, e / (1 + e) below.
+__device__ __forceinline__ float softplus_sig(float v, float& sig) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+    const float u = 1.0f + e;
+    const float lost = e - (u - 1.0f);
+    const float r = __builtin_amdgcn_rcpf(u);
+    sig = v >= 0.0f ? r : e * r;
+    return fmaxf(v, 0.0f) + fmaf(__builtin_amdgcn_logf(u), kLn2, lost);
+}
+
 // silu(z) = z / (1 + exp(-z)); exp overflow gives 1/inf = 0 and a signed zero.
 __device__ __forceinline__ float silu(float z) {
     const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
@@ -84,9 +95,45 @@ struct S6StepArgs {
     int bf16;
 };
 
+struct S6BwdArgs {
+    const void* x; const void* delta; const void* z;
+    const void* B; const void* C; const void* dout;
+    const float* A; const float* Dskip; const float* dt_bias;
+    const float* h0; const float* dh_last;
+    void* dx; void* ddelta; void* dz;
+    float* dB; float* dC;            // (batch, L, N)
+    float* dA; float* dDskip; float* ddt_bias;
+    float* dh0;                      // (batch, D, N) or NULL
+    // workspace
+    float* carry_S; float* carry_H;      // forward carries / starting states, (batch, n-1, [N,] D)
+    float* rcarry_S; float* rcarry_H;    // adjoint carries / incoming adjoints, same shapes
+    float* ckpt;                         // (batch, n, chunk_len / sub, N, D) sub-chunk starting states
+    float* part_bc;                      // (batch, L, ceil(D / 64), 2N) per-wavefront dB | dC sums
+    float* part_p;                       // (batch, n, N + 2, D) per-chunk dA | dDskip | ddt_bias
+    int64_t batch, L, D;
+    int64_t chunk_len, n_chunks;
+    int bf16;
+    int pair_loads;
+};
+
+// In-order combine of chunk carries (S = sum of Delta, H = state), in place.
+struct S6FoldArgs {
+    const float* A;
+    const float* init;   // (batch, D, N) starting value, NULL = zero
+    float* S;            // (batch, ncar, D)
+    float* H;            // (batch, ncar, N, D); overwritten with the prefixes
+    int64_t batch, D, ncar;
+    int reverse;         // fold carries ncar-1 .. 0 instead of 0 .. ncar-1
+};
+
 // Optional per-launch timing (ssm_timing_enable): called before and after
 // every kernel launch with the launch's stream.
 void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin);
 
 hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream);
+void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream);
+void s6_launch_chunk_carry(const S6ScanArgs& a, hipStream_t stream);   // chunks 0 .. n-2
+hipError_t s6_launch_bwd(const S6BwdArgs& a, hipStream_t stream);
+constexpr int kBwdSub = 4;           // tokens per backward sub-chunk (states kept in registers)
+constexpr int kBwdParams = 18;       // dA (16), dDskip, ddt_bias partials per lane and chunk
 hipError_t s6_launch_step(const S6StepArgs& a, hipStream_t stream);

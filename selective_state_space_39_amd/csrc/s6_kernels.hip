@@ -32,197 +32,9 @@
 // as the VGPR offset and the token's row offset as one SGPR offset shared by
 // all four tensors, so the token loop does no per-lane address arithmetic.
 
-#include "s6_common.h"
+#include "s6_device.h"
 
 namespace s6 {
-
-// ---------------------------------------------------------------------------
-// B_t / C_t rows through the scalar cache
-// ---------------------------------------------------------------------------
-typedef const __attribute__((address_space(4))) uint32_t cu32;
-
-template <class IO> struct RowBC;
-
-template <> struct RowBC<BF16> {
-    uint32_t w[8];    // 16 bf16 values, two per word
-    __device__ __forceinline__ void load(const uint16_t* row) {
-        cu32* p = (cu32*)row;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = p[i];
-    }
-    __device__ __forceinline__ float get(int n) const {
-        return (n & 1) ? bf16_hi(w[n >> 1]) : bf16_lo(w[n >> 1]);
-    }
-};
-
-template <> struct RowBC<F32> {
-    uint32_t w[16];
-    __device__ __forceinline__ void load(const float* row) {
-        cu32* p = (cu32*)row;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = p[i];
-    }
-    __device__ __forceinline__ float get(int n) const { return __uint_as_float(w[n]); }
-};
-
-// Scalar loads can return out of order, so any wait on them is a wait for all
-// of them.  Waiting here, before the next token's B/C loads are issued, keeps
-// those loads in flight across the whole token instead of stalling on them.
-__device__ __forceinline__ void lgkm_wait_all() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // vmcnt/expcnt untouched, lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// ---------------------------------------------------------------------------
-// one (batch, L, D) io tensor, restricted to a chunk, as a buffer resource
-// ---------------------------------------------------------------------------
-constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format (gfx9 family)
-
-template <class IO> struct ChunkIO {
-    __amdgpu_buffer_rsrc_t r;
-    __device__ __forceinline__ void init(const void* chunk_base, uint32_t bytes) {
-        r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(chunk_base), 0, static_cast<int>(bytes),
-                                              kRsrcWord3);
-    }
-};
-
-// Element loaders of x, delta and z.  load() returns raw bits that stay in
-// the prefetch ring; widen() turns them into fp32 where they are used.  The
-// ring must hold plain 32-bit values: anything the compiler has to do to a
-// loaded value before the loop back-edge (zero-extend, pack two 16-bit values
-// into one register) makes it wait for the whole ring.
-//   LdPairBF16 (bf16, D even, 4-byte aligned io): each lane loads the aligned
-//     dword that holds its element (two lanes share it) and picks its half
-//     with one byte permute at use.
-//   LdBF16: 16-bit loads (any D); the compiler packs the ring, which costs a
-//     wait per ring turn.
-//   LdF32: 32-bit loads.
-struct LdPairBF16 {
-    using IO = BF16;
-    using R = uint32_t;
-    uint32_t sel;                                   // byte-permute selector of this lane's half
-    __device__ __forceinline__ uint32_t voff(uint32_t d) {
-        sel = (d & 1u) ? 0x03020c0cu : 0x01000c0cu;
-        return (d * 2u) & ~3u;
-    }
-    __device__ __forceinline__ R load(const ChunkIO<BF16>& s, uint32_t vo, uint32_t so) const {
-        return __builtin_amdgcn_raw_buffer_load_b32(s.r, vo, so, 0);
-    }
-    __device__ __forceinline__ float widen(R w) const { return __uint_as_float(__builtin_amdgcn_perm(0u, w, sel)); }
-};
-
-struct LdBF16 {
-    using IO = BF16;
-    using R = uint16_t;
-    __device__ __forceinline__ uint32_t voff(uint32_t d) { return d * 2u; }
-    __device__ __forceinline__ R load(const ChunkIO<BF16>& s, uint32_t vo, uint32_t so) const {
-        return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(s.r, vo, so, 0));
-    }
-    __device__ __forceinline__ float widen(R u) const { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
-};
-
-struct LdF32 {
-    using IO = F32;
-    using R = uint32_t;
-    __device__ __forceinline__ uint32_t voff(uint32_t d) { return d * 4u; }
-    __device__ __forceinline__ R load(const ChunkIO<F32>& s, uint32_t vo, uint32_t so) const {
-        return __builtin_amdgcn_raw_buffer_load_b32(s.r, vo, so, 0);
-    }
-    __device__ __forceinline__ float widen(R u) const { return __uint_as_float(u); }
-};
-
-__device__ __forceinline__ void store_io(const ChunkIO<BF16>& s, uint32_t voff, uint32_t soff, float v) {
-    const __bf16 b = static_cast<__bf16>(v);                  // round to nearest even
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), s.r, voff, soff, 0);
-}
-__device__ __forceinline__ void store_io(const ChunkIO<F32>& s, uint32_t voff, uint32_t soff, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), s.r, voff, soff, 0);
-}
-
-// ---------------------------------------------------------------------------
-// lane / chunk geometry
-// ---------------------------------------------------------------------------
-struct Geo {
-    uint32_t d;        // channel; lanes past D take D-1 and duplicate its (identical) results
-    int b, c;          // batch row, chunk
-    int t0, nt;        // first token and token count of the chunk
-    int64_t row0;      // b * L + t0: token row of the chunk start
-};
-
-// The wavefront index is made wave-uniform explicitly, so the early exit and
-// every bound derived after it stay in SGPRs.
-constexpr int kXcds = 8;
-
-// Linear workgroup index -> (channel block, chunk, batch row).  The launch is
-// a 1-D grid of nblk * nchunks workgroups (nblk = channel blocks x batch
-// rows, batch-row major).  When nblk is a multiple of the XCD count,
-// workgroup i runs on XCD i % 8 at position i / 8 there; XCD x is given the
-// contiguous channel blocks [x * nblk/8, (x+1) * nblk/8) with all their
-// chunks, so a batch row's B/C rows are shared in one L2 and every carry is
-// read on the XCD that wrote it.  Otherwise the plain row-major order is used.
-__device__ __forceinline__ void wg_coords(int64_t nblk, int64_t nchunks, int64_t& blk, int64_t& chunk) {
-    const int64_t i = blockIdx.x;
-    if (nblk % kXcds == 0) {
-        const int64_t xcd = i % kXcds, pos = i / kXcds;
-        blk = xcd * (nblk / kXcds) + pos / nchunks;
-        chunk = pos % nchunks;
-    } else {
-        blk = i % nblk;
-        chunk = i / nblk;
-    }
-}
-
-__device__ __forceinline__ bool geo_setup(const S6ScanArgs& a, int64_t nchunks, Geo& g) {
-    const int64_t gx = (a.D + kBlock - 1) / kBlock;            // channel blocks per batch row
-    int64_t blk, chunk;
-    wg_coords(gx * a.batch, nchunks, blk, chunk);
-    const int64_t bx = blk % gx;
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int64_t first = bx * kBlock + wave * kWave;
-    if (first >= a.D) return false;               // whole wavefront past the last channel
-    const int64_t d = first + (threadIdx.x & (kWave - 1));
-    g.d = static_cast<uint32_t>(d < a.D ? d : a.D - 1);
-    g.c = static_cast<int>(chunk);
-    g.b = static_cast<int>(blk / gx);
-    g.t0 = g.c * static_cast<int>(a.chunk_len);
-    const int t1 = g.t0 + static_cast<int>(a.chunk_len);
-    g.nt = (t1 < a.L ? t1 : static_cast<int>(a.L)) - g.t0;
-    g.row0 = static_cast<int64_t>(g.b) * a.L + g.t0;
-    return true;
-}
-
-// x, delta (and z) are double-buffered in registers in blocks of kBlk tokens:
-// while a wavefront computes block k from fp32 values v, the global loads of
-// block k+1 are in flight into raw registers r; after the compute, r is
-// widened into v.  No value whose load is still in flight is live across the
-// loop back-edge, so the only wait for the loads is that widening, once per
-// block, after a whole block of compute.  Load offsets are clamped to the
-// chunk's last token; tokens past the chunk end (only in a ragged last chunk)
-// are masked: Delta = 0 leaves the state unchanged, and they are not stored.
-constexpr int kBlk = 4;
-
-template <class LD, int NT>
-struct Stage {
-    using IO = typename LD::IO;
-    typename LD::R r[NT][kBlk];                    // raw loads of the next block, in flight
-    float v[NT][kBlk];                             // fp32 values of the current block
-
-    __device__ __forceinline__ void issue(const LD& ld, const ChunkIO<IO> (&src)[NT], uint32_t vo,
-                                          uint32_t first, uint32_t rowb, uint32_t last) {
-#pragma unroll
-        for (int j = 0; j < kBlk; ++j) {
-            const uint32_t o = min(first + static_cast<uint32_t>(j) * rowb, last);
-#pragma unroll
-            for (int k = 0; k < NT; ++k) r[k][j] = ld.load(src[k], vo, o);
-        }
-    }
-    __device__ __forceinline__ void widen(const LD& ld) {
-#pragma unroll
-        for (int k = 0; k < NT; ++k)
-#pragma unroll
-            for (int j = 0; j < kBlk; ++j) v[k][j] = ld.widen(r[k][j]);
-    }
-};
 
 // ---------------------------------------------------------------------------
 // phase 1: chunk carries
@@ -235,7 +47,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
     LD ld;
     constexpr uint32_t es = sizeof(T);
     Geo g;
-    if (!geo_setup(a, a.n_chunks - 1, g)) return;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks - 1, 0, g)) return;
     const uint32_t rowb = static_cast<uint32_t>(a.D) * es;       // bytes per token row
     const uint32_t last = static_cast<uint32_t>(g.nt - 1) * rowb;
     const int64_t e0 = g.row0 * a.D;                             // element offset of the chunk
@@ -289,11 +101,14 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
 // One wavefront per (batch row, 64 channels, state n): lanes are channels, so
 // every carry read and every prefix write is one coalesced 256-byte row.  The
 // carries of up to kScanBlk chunks are loaded at once, then combined in
-// order: h <- exp(A_n S_c) h + H_c, starting from h0.  The combined prefix
-// after chunk c is the starting state of chunk c+1 and overwrites H_c.
+// order: h <- exp(A_n S_c) h + H_c, starting from `init` (zero when NULL).
+// The combined prefix after carry c overwrites H_c.  The forward scan folds
+// carries in chunk order from h0 (prefix c = starting state of chunk c+1);
+// the backward pass folds its adjoint carries in reverse order from dh_last
+// (the same combine: the adjoint obeys the transposed recurrence).
 constexpr int kScanBlk = 16;
 
-__global__ __launch_bounds__(kBlock) void s6_carry_scan(S6ScanArgs a) {
+__global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t gx = (a.D + kWave - 1) / kWave;               // 64-channel groups per batch row
     const int64_t unit = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave;
@@ -304,25 +119,27 @@ __global__ __launch_bounds__(kBlock) void s6_carry_scan(S6ScanArgs a) {
     const int64_t first = (grp % gx) * kWave;
     const int64_t dl = first + (threadIdx.x & (kWave - 1));
     const int64_t d = dl < a.D ? dl : a.D - 1;
-    const int64_t ncar = a.n_chunks - 1;
+    const int64_t ncar = a.ncar;
     const float A2 = a.A[d * kN + n] * kLog2e;
-    float h = a.h0 ? a.h0[(b * a.D + d) * kN + n] : 0.0f;
-    const float* S = a.carry_S + b * ncar * a.D + d;
-    float* H = a.carry_H + (b * ncar * kN + n) * a.D + d;
-    const int64_t hs = kN * a.D;                                // H stride between chunks
-    for (int64_t c0 = 0; c0 < ncar; c0 += kScanBlk) {
+    float h = a.init ? a.init[(b * a.D + d) * kN + n] : 0.0f;
+    const float* S = a.S + b * ncar * a.D + d;
+    float* H = a.H + (b * ncar * kN + n) * a.D + d;
+    const int64_t hs = kN * a.D;                                // H stride between carries
+    for (int64_t k0 = 0; k0 < ncar; k0 += kScanBlk) {
         float Sv[kScanBlk], Hv[kScanBlk];
 #pragma unroll
         for (int k = 0; k < kScanBlk; ++k) {
-            const int64_t c = c0 + k < ncar ? c0 + k : ncar - 1;
+            const int64_t kk = k0 + k < ncar ? k0 + k : ncar - 1;
+            const int64_t c = a.reverse ? ncar - 1 - kk : kk;
             Sv[k] = S[c * a.D];
             Hv[k] = H[c * hs];
         }
 #pragma unroll
         for (int k = 0; k < kScanBlk; ++k) {
-            if (c0 + k < ncar) {                                  // wave-uniform
+            if (k0 + k < ncar) {                                  // wave-uniform
+                const int64_t c = a.reverse ? ncar - 1 - (k0 + k) : k0 + k;
                 h = fmaf(__builtin_amdgcn_exp2f(A2 * Sv[k]), h, Hv[k]);
-                H[(c0 + k) * hs] = h;
+                H[c * hs] = h;
             }
         }
     }
@@ -339,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
     LD ld;
     constexpr uint32_t es = sizeof(T);
     Geo g;
-    if (!geo_setup(a, a.n_chunks, g)) return;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks, 0, g)) return;
     const int64_t D = a.D;
     const uint32_t rowb = static_cast<uint32_t>(D) * es;
     const uint32_t last = static_cast<uint32_t>(g.nt - 1) * rowb;
@@ -487,17 +304,31 @@ static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
         s6_timing_mark("s6_chunk_carry", stream, true);
         hipLaunchKernelGGL(s6_chunk_carry<LD>, g1, dim3(kBlock), 0, stream, a);
         s6_timing_mark("s6_chunk_carry", stream, false);
-        const int64_t waves = a.batch * ((a.D + kWave - 1) / kWave) * kN;
-        dim3 g2(static_cast<unsigned>((waves + kBlock / kWave - 1) / (kBlock / kWave)));
-        s6_timing_mark("s6_carry_scan", stream, true);
-        hipLaunchKernelGGL(s6_carry_scan, g2, dim3(kBlock), 0, stream, a);
-        s6_timing_mark("s6_carry_scan", stream, false);
+        S6FoldArgs f{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0};
+        s6_launch_fold(f, "s6_carry_scan", stream);
     }
     dim3 g3(static_cast<unsigned>(nblk * a.n_chunks));
     s6_timing_mark("s6_chunk_out", stream, true);
     hipLaunchKernelGGL((s6_chunk_out<LD, GATED>), g3, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_chunk_out", stream, false);
     return hipGetLastError();
+}
+
+void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
+    const int64_t waves = f.batch * ((f.D + kWave - 1) / kWave) * kN;
+    dim3 g(static_cast<unsigned>((waves + kBlock / kWave - 1) / (kBlock / kWave)));
+    s6_timing_mark(name, stream, true);
+    hipLaunchKernelGGL(s6_carry_scan, g, dim3(kBlock), 0, stream, f);
+    s6_timing_mark(name, stream, false);
+}
+
+void s6_launch_chunk_carry(const S6ScanArgs& a, hipStream_t stream) {
+    dim3 g1(static_cast<unsigned>((a.D + kBlock - 1) / kBlock * a.batch * (a.n_chunks - 1)));
+    s6_timing_mark("s6_chunk_carry", stream, true);
+    if (a.bf16 && a.pair_loads) hipLaunchKernelGGL(s6_chunk_carry<LdPairBF16>, g1, dim3(kBlock), 0, stream, a);
+    else if (a.bf16) hipLaunchKernelGGL(s6_chunk_carry<LdBF16>, g1, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL(s6_chunk_carry<LdF32>, g1, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_chunk_carry", stream, false);
 }
 
 hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream) {

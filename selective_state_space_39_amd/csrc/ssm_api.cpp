@@ -150,6 +150,52 @@ int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
     return SSM_OK;
 }
 
+// Backward plan: its dominant kernel holds three wavefronts per SIMD, so the
+// automatic chunk length aims at about four such wavefronts per SIMD in total.
+struct BwdPlan {
+    int64_t chunk_len, n_chunks;
+    int64_t off_carry_S, off_carry_H, off_rcarry_S, off_rcarry_H, off_ckpt, off_bc, off_p;
+    int64_t ws_bytes;
+};
+
+constexpr int64_t kBwdTargetWaves = 4 * kSimds;
+
+int make_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, BwdPlan& p) {
+    if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
+        return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
+                    (long long)chunk_len, (long long)kChunkAlign);
+    if (chunk_len == 0) {
+        const int64_t groups = batch * ((D + 63) / 64);
+        const int64_t max_chunks = (L + kChunkAlign - 1) / kChunkAlign;
+        int64_t n = std::min(std::max<int64_t>((kBwdTargetWaves + groups - 1) / groups, 1), max_chunks);
+        chunk_len = ((L + n - 1) / n + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    }
+    p.chunk_len = chunk_len;
+    p.n_chunks = (L + chunk_len - 1) / chunk_len;
+    if (p.n_chunks > kMaxGrid)
+        return fail(SSM_ERR_SHAPE, "%lld chunks exceed %lld; use a longer chunk_len",
+                    (long long)p.n_chunks, (long long)kMaxGrid);
+    if (batch * ((D + 255) / 256) * p.n_chunks > (int64_t(1) << 31) - 1)
+        return fail(SSM_ERR_SHAPE, "batch * ceil(D / 256) * chunks exceeds the grid limit");
+    auto part = [](int64_t floats) { return floats < 0 ? int64_t(-1) : (floats * 4 + 255) / 256 * 256; };
+    const int64_t carries = mul_ck(mul_ck(batch, p.n_chunks - 1), D);
+    const int64_t ckpt = mul_ck(mul_ck(mul_ck(mul_ck(batch, p.n_chunks), chunk_len / kBwdSub), kN), D);
+    const int64_t bc = mul_ck(mul_ck(mul_ck(batch, L), (D + 63) / 64), 2 * kN);
+    const int64_t pp = mul_ck(mul_ck(mul_ck(batch, p.n_chunks), kBwdParams), D);
+    const int64_t sizes[7] = {part(carries), part(mul_ck(carries, kN)), part(carries), part(mul_ck(carries, kN)),
+                              part(ckpt), part(bc), part(pp)};
+    int64_t* offs[7] = {&p.off_carry_S, &p.off_carry_H, &p.off_rcarry_S, &p.off_rcarry_H, &p.off_ckpt,
+                        &p.off_bc, &p.off_p};
+    int64_t at = 0;
+    for (int i = 0; i < 7; ++i) {
+        if (sizes[i] < 0 || at > kMaxBytes - sizes[i]) return fail(SSM_ERR_SHAPE, "workspace size overflows");
+        *offs[i] = at;
+        at += (i < 4 && p.n_chunks == 1) ? 0 : sizes[i];
+    }
+    p.ws_bytes = at;
+    return SSM_OK;
+}
+
 // ---------------------------------------------------------------------------
 // per-kernel timing
 // ---------------------------------------------------------------------------
@@ -329,6 +375,107 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
     a.bf16 = io_dtype == SSM_BF16;
     a.pair_loads = a.bf16 && D % 2 == 0 && aligned(x, 4) && aligned(delta, 4) && (!z || aligned(z, 4));
     hipError_t e = s6_launch_scan(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                                     int64_t chunk_len) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    BwdPlan p;
+    rc = make_bwd_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+    ok();
+    return p.ws_bytes;
+}
+
+int ssm_scan_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype, int64_t chunk_len,
+                      int64_t* chunk_len_out, int64_t* n_chunks_out) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    BwdPlan p;
+    rc = make_bwd_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+    if (chunk_len_out) *chunk_len_out = p.chunk_len;
+    if (n_chunks_out) *n_chunks_out = p.n_chunks;
+    return ok();
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                 const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                 const void* dout, const float* dh_last,
+                 void* dx, void* ddelta, void* dz, float* dB, float* dC,
+                 float* dA, float* dDskip, float* ddt_bias, float* dh0,
+                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                 int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = check_shape(batch, L, D, N, io_dtype);
+    if (rc) return rc;
+    BwdPlan p;
+    rc = make_bwd_plan(batch, L, D, chunk_len, p);
+    if (rc) return rc;
+
+    struct { const void* p; const char* n; } req[] = {
+        {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"}, {dt_bias, "dt_bias"},
+        {dout, "dout"}, {dx, "dx"}, {ddelta, "ddelta"}, {dB, "dB"}, {dC, "dC"}, {dA, "dA"},
+        {dDskip, "dDskip"}, {ddt_bias, "ddt_bias"}};
+    for (auto& r : req)
+        if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    if ((z == nullptr) != (dz == nullptr))
+        return fail(SSM_ERR_NULL, "z and dz must both be given (gated) or both be NULL (ungated)");
+    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)p.ws_bytes);
+    if (workspace_bytes < p.ws_bytes)
+        return fail(SSM_ERR_WORKSPACE, "workspace has %lld bytes; %lld needed", (long long)workspace_bytes,
+                    (long long)p.ws_bytes);
+
+    const int64_t es = esize(io_dtype);
+    struct { const void* p; int64_t a; const char* n; } al[] = {
+        {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {B, 16, "B"}, {C, 16, "C"}, {dout, es, "dout"},
+        {dx, es, "dx"}, {ddelta, es, "ddelta"}, {dz, es, "dz"}, {A, 4, "A"}, {Dskip, 4, "Dskip"},
+        {dt_bias, 4, "dt_bias"}, {h0, 4, "h0"}, {dh_last, 4, "dh_last"}, {dB, 4, "dB"}, {dC, 4, "dC"},
+        {dA, 4, "dA"}, {dDskip, 4, "dDskip"}, {ddt_bias, 4, "ddt_bias"}, {dh0, 4, "dh0"},
+        {workspace, 256, "workspace"}};
+    for (auto& r : al)
+        if (r.p && !aligned(r.p, r.a))
+            return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
+
+    const int64_t seq = batch * L * D * es, bc = batch * L * kN * es, st = batch * D * kN * 4;
+    const int64_t bcf = batch * L * kN * 4;
+    const Range ins[] = {rng("x", x, seq), rng("delta", delta, seq), rng("z", z, seq), rng("B", B, bc),
+                         rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
+                         rng("dt_bias", dt_bias, D * 4), rng("h0", h0, st), rng("dout", dout, seq),
+                         rng("dh_last", dh_last, st), rng("workspace", workspace, p.ws_bytes)};
+    const Range outs[] = {rng("dx", dx, seq), rng("ddelta", ddelta, seq), rng("dz", dz, seq),
+                          rng("dB", dB, bcf), rng("dC", dC, bcf), rng("dA", dA, D * kN * 4),
+                          rng("dDskip", dDskip, D * 4), rng("ddt_bias", ddt_bias, D * 4), rng("dh0", dh0, st)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (auto& in : ins)
+            if (overlap(outs[i], in)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, in.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+
+    S6BwdArgs a{};
+    a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.dout = dout;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0; a.dh_last = dh_last;
+    a.dx = dx; a.ddelta = ddelta; a.dz = dz; a.dB = dB; a.dC = dC;
+    a.dA = dA; a.dDskip = dDskip; a.ddt_bias = ddt_bias; a.dh0 = dh0;
+    char* ws = static_cast<char*>(workspace);
+    if (p.n_chunks > 1) {
+        a.carry_S = reinterpret_cast<float*>(ws + p.off_carry_S);
+        a.carry_H = reinterpret_cast<float*>(ws + p.off_carry_H);
+        a.rcarry_S = reinterpret_cast<float*>(ws + p.off_rcarry_S);
+        a.rcarry_H = reinterpret_cast<float*>(ws + p.off_rcarry_H);
+    }
+    a.ckpt = reinterpret_cast<float*>(ws + p.off_ckpt);
+    a.part_bc = reinterpret_cast<float*>(ws + p.off_bc);
+    a.part_p = reinterpret_cast<float*>(ws + p.off_p);
+    a.batch = batch; a.L = L; a.D = D;
+    a.chunk_len = p.chunk_len; a.n_chunks = p.n_chunks;
+    a.bf16 = io_dtype == SSM_BF16;
+    a.pair_loads = a.bf16 && D % 2 == 0 && aligned(x, 4) && aligned(delta, 4) && aligned(dout, 4) &&
+                   (!z || aligned(z, 4));
+    hipError_t e = s6_launch_bwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -174,12 +174,15 @@ def block_delta(rng, batch, L, D, dt_bias, block=64, lo=1e-3, hi=1.0, jitter=0.1
 
 def make_scan_inputs(batch: int, L: int, D: int, N: int = N_STATE, io: str = "bf16",
                      seed=(SEED_ROOT, 0), delta: str = "normal", delta_sigma: float = 0.5,
-                     block: int = 64, gated: bool = True, with_h0: bool = False) -> ScanInputs:
+                     block: int = 64, gated: bool = True, with_h0: bool = False,
+                     A_random: bool = False) -> ScanInputs:
     """Seeded inputs for one whole-sequence scan.
 
     Draw order from ``numpy.random.default_rng(seed)``: u (-> dt_bias), x,
     delta (or the block-jitter eps), z, B, C, h0. x, z, B, C ~ N(0, 1);
     delta ~ N(0, delta_sigma^2) or the alternating blocks; h0 ~ N(0, 1).
+    With ``A_random`` the S4D-real A is replaced by A_dn = -exp(U(-1.5, 1.5)),
+    different for every channel and state, drawn from the stream (*seed, 2).
     """
     rng = np.random.default_rng(list(seed) if not isinstance(seed, int) else seed)
     A, Dskip, dt_bias = channel_params(rng, D, N)
@@ -194,10 +197,32 @@ def make_scan_inputs(batch: int, L: int, D: int, N: int = N_STATE, io: str = "bf
     B = _normal(rng, (batch, L, N))
     C = _normal(rng, (batch, L, N))
     h0 = _normal(rng, (batch, D, N)) if with_h0 else None
+    if A_random:
+        ra = np.random.default_rng(list(seed) + [2] if not isinstance(seed, int) else [seed, 2])
+        A = (-np.exp(ra.uniform(-1.5, 1.5, size=(D, N)))).astype(np.float32)
     return ScanInputs(io=io, x=_as_io(x, io), delta=_as_io(dl, io),
                       z=None if z is None else _as_io(z, io),
                       B=_as_io(B, io), C=_as_io(C, io), A=A, Dskip=Dskip, dt_bias=dt_bias,
                       h0=h0, meta=dict(seed=seed, delta=delta))
+
+
+@dataclass
+class GradOutputs:
+    io: str
+    dout: np.ndarray                  # (batch, L, D) io storage: gradient of the scan output
+    dh_last: Optional[np.ndarray]     # (batch, D, N) float32: gradient of the final state, or None
+
+
+def make_grad_outputs(batch: int, L: int, D: int, N: int = N_STATE, io: str = "bf16", seed=(SEED_ROOT, 0),
+                      with_dh_last: bool = True) -> GradOutputs:
+    """Upstream gradients for a backward pass, from the stream (*seed, 1).
+
+    Draw order: dout ~ N(0, 1) (rounded to the io dtype), dh_last ~ N(0, 1).
+    """
+    rng = np.random.default_rng(list(seed) + [1] if not isinstance(seed, int) else [seed, 1])
+    dout = _normal(rng, (batch, L, D))
+    dh = _normal(rng, (batch, D, N)) if with_dh_last else None
+    return GradOutputs(io=io, dout=_as_io(dout, io), dh_last=dh)
 
 
 def make_config(k: int) -> ScanInputs:

@@ -66,3 +66,57 @@ def assert_close(a, ref, tol, what):
     assert np.all(np.isfinite(a)), f"{what}: non-finite values"
     assert e <= tol, f"{what}: {e:.3e} > {tol:.0e}"
     return e
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+GRAD_KEYS = ("x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0")
+
+
+def gpu_bwd(s: inputs.ScanInputs, go: inputs.GradOutputs, chunk_len=0, gated=True, h0=True, want_dh0=True):
+    io = s.io
+    g = binding.scan_bwd(dev(s.x, io), dev(s.delta, io), f32dev(s.A), dev(s.B, io), dev(s.C, io),
+                         f32dev(s.Dskip), f32dev(s.dt_bias), dev(go.dout, io),
+                         z=dev(s.z, io) if gated else None, h0=f32dev(s.h0) if h0 else None,
+                         dh_last=f32dev(go.dh_last), chunk_len=chunk_len, want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_bwd(s: inputs.ScanInputs, go: inputs.GradOutputs, gated=True, h0=True, strip=None):
+    """oracle.scan_bwd on the same bits; with `strip`, channel strips at a time (dB and dC summed)."""
+    D = s.x.shape[2]
+    strip = strip or D
+    out = None
+    for d0 in range(0, D, strip):
+        sel = slice(d0, min(D, d0 + strip))
+        r = oracle.scan_bwd(s.x[:, :, sel], s.delta[:, :, sel], s.A[sel], s.B, s.C, s.Dskip[sel], s.dt_bias[sel],
+                            go.dout[:, :, sel], z=s.z[:, :, sel] if gated else None,
+                            h0=s.h0[:, sel] if (h0 and s.h0 is not None) else None,
+                            dh_last=None if go.dh_last is None else go.dh_last[:, sel], io=s.io)
+        if out is None:
+            out = {k: (None if v is None else [v]) for k, v in r.items()}
+            continue
+        for k, v in r.items():
+            if v is not None:
+                out[k].append(v)
+    axis = {"x": 2, "delta": 2, "z": 2, "A": 0, "Dskip": 0, "dt_bias": 0, "h0": 1}
+    res = {}
+    for k, parts in out.items():
+        if parts is None:
+            res[k] = None
+        elif k in ("B", "C"):
+            res[k] = np.sum(parts, axis=0)
+        else:
+            res[k] = np.concatenate(parts, axis=axis[k])
+    return res
+
+
+def assert_grads_close(g, ref, tol, what, keys=GRAD_KEYS):
+    for k in keys:
+        if ref.get(k) is None:
+            assert g.get(k) is None, f"{what}: d{k} should be absent"
+            continue
+        assert_close(host64(g[k]), ref[k], tol, f"{what} d{k}")

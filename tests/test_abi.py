@@ -147,3 +147,90 @@ def test_binding_rejects_bad_tensors_on_cpu():
     x = torch.zeros(1, 4, 8, dtype=torch.float16)
     with pytest.raises(TypeError):
         binding.scan_fwd(x, x, torch.zeros(8, 16), x, x, torch.zeros(8), torch.zeros(8))
+
+
+# ---------------------------------------------------------------------------
+# backward entry points
+# ---------------------------------------------------------------------------
+
+def _part(floats):
+    return (floats * 4 + 255) // 256 * 256
+
+
+def test_bwd_plan_and_workspace():
+    # (batch, L, D) = (2, 300, 200), 64-token chunks: 5 chunks, 4 carries per row
+    assert binding.bwd_plan(2, 300, 200, 1, 64) == (64, 5)
+    carries = 2 * 4 * 200
+    expect = (2 * (_part(carries) + _part(carries * 16))     # state and adjoint carries
+              + _part(2 * 5 * (64 // 4) * 16 * 200)          # sub-chunk checkpoints
+              + _part(2 * 300 * 4 * 32)                      # per-wavefront dB | dC sums
+              + _part(2 * 5 * 18 * 200))                     # per-chunk parameter sums
+    assert binding.bwd_workspace_bytes(2, 300, 200, 1, 64) == expect
+    # one chunk: no carries, still checkpoints and partial sums
+    cl, nc = binding.bwd_plan(1, 40, 16, 0, 64)
+    assert (cl, nc) == (64, 1)
+    assert binding.bwd_workspace_bytes(1, 40, 16, 0, 64) == (_part(64 // 4 * 16 * 16) + _part(40 * 1 * 32)
+                                                              + _part(18 * 16))
+    for (b, l, d) in [(8, 2048, 1536), (4, 2048, 5120), (1, 131072, 2048), (1, 256, 16)]:
+        cl, nc = binding.bwd_plan(b, l, d, 1, 0)
+        assert cl % 32 == 0 and nc == -(-l // cl) and nc >= 1
+    L = binding.lib()
+    assert L.ssm_scan_bwd_workspace_bytes(1, 10, 8, 16, 1, 48) == E_SHAPE
+    assert L.ssm_scan_bwd_workspace_bytes(1, 10, 8, 8, 1, 0) == E_N
+
+
+BWD_ARGS = ["x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "dout", "dh_last",
+            "dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"]
+
+
+class FakeBwd:
+    def __init__(self, batch=2, L=64, D=128, io=1):
+        es = 2 if io == 1 else 4
+        seq, bc, st = batch * L * D * es, batch * L * 16 * es, batch * D * 64
+        self.sizes = dict(x=seq, delta=seq, z=seq, B=bc, C=bc, A=D * 64, Dskip=D * 4, dt_bias=D * 4, h0=st,
+                          dout=seq, dh_last=st, dx=seq, ddelta=seq, dz=seq, dB=batch * L * 64,
+                          dC=batch * L * 64, dA=D * 64, dDskip=D * 4, ddt_bias=D * 4, dh0=st, ws=64 << 20)
+        addr = 1 << 40
+        self.p = {}
+        for k, n in self.sizes.items():
+            self.p[k] = addr
+            addr += (n + 4095) // 4096 * 4096 + 4096
+        self.batch, self.L, self.D, self.io = batch, L, D, io
+
+    def call(self, chunk_len=32, ws_bytes=64 << 20, **over):
+        p = dict(self.p)
+        p.update(over)
+        v = lambda k: ctypes.c_void_p(p[k]) if p[k] is not None else None
+        return binding.lib().ssm_scan_bwd(*[v(k) for k in BWD_ARGS], self.batch, self.L, self.D, 16, self.io,
+                                          chunk_len, v("ws"), ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "B", "C", "A", "Dskip", "dt_bias", "dout", "dx", "ddelta",
+                                  "dB", "dC", "dA", "dDskip", "ddt_bias"])
+def test_bwd_null_required(name):
+    assert FakeBwd().call(**{name: None}) == E_NULL
+    assert name in binding.lib().ssm_last_error().decode()
+
+
+def test_bwd_gate_pairing_and_workspace():
+    f = FakeBwd()
+    assert f.call(dz=None) == E_NULL          # gated scan needs dz
+    assert f.call(z=None) == E_NULL           # dz without z
+    assert f.call(ws=None) == E_WS
+    assert f.call(ws_bytes=100) == E_WS
+    assert f.call(chunk_len=40) == E_SHAPE
+
+
+@pytest.mark.parametrize("name,off", [("dout", 1), ("dx", 1), ("dz", 1), ("dB", 2), ("dA", 2), ("dh0", 2),
+                                      ("dh_last", 1), ("ws", 128)])
+def test_bwd_alignment(name, off):
+    f = FakeBwd()
+    assert f.call(**{name: f.p[name] + off}) == E_ALIGN
+
+
+@pytest.mark.parametrize("out,inp", [("dx", "x"), ("ddelta", "dout"), ("dz", "z"), ("dB", "B"), ("dC", "ws"),
+                                     ("dA", "A"), ("dh0", "h0"), ("dh0", "dh_last"), ("dx", "ddelta"),
+                                     ("dDskip", "dA"), ("ddt_bias", "dDskip")])
+def test_bwd_alias(out, inp):
+    f = FakeBwd()
+    assert f.call(**{out: f.p[inp]}) == E_ALIAS
