@@ -44,9 +44,21 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12        # 78.64, fp32 vector without packed math
 SLOTS_PER_ELEMENT = 112
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
-WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5}
+WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5,
+             "mamba-130m-layer-bwd": 2, "mamba-2.8b-layer-bwd": 3}
+# Backward: algorithmic fp32 VALU issue slots per element (b, t, d), exp/log/rcp counted as 2:
+#   state recompute: softplus 7 + Delta*x 1 + 16 x (mul, exp, mul, fma) 80           = 88
+#   readout for the gate gradient: 16 FMA + skip                                       = 17
+#   gate gradient (sigmoid, silu, derivative)                                          =  9
+#   adjoint step: 16 x (mu, du, dC term, mul, exp, q, w, sum w A, dA, dB term)          = 176
+#   per-token tail: sigmoid(v) from the softplus exponential, dx, dDelta, ddelta, dD, dbias = 10
+#   channel sums of dB and dC: one add per value per channel                           = 32
+BWD_SLOTS_PER_ELEMENT = 332
+BWD_DOMINANT = "s6_chunk_bwd"
 KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/s6_kernels.hip",
+                  "selective_state_space_39_amd/csrc/s6_device.h",
                   "selective_state_space_39_amd/csrc/s6_common.h"]
+BWD_KERNEL_SOURCES = KERNEL_SOURCES + ["selective_state_space_39_amd/csrc/s6_bwd.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -55,9 +67,10 @@ def algorithmic_bytes(batch, L, D, N=16, io_bytes=2):
     return (4 * batch * L * D * io_bytes + 2 * batch * L * N * io_bytes + D * (N + 2) * 4 + batch * D * N * 4)
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload=""):
+    """Hash of the sources the workload's kernels are compiled from."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (BWD_KERNEL_SOURCES if workload.endswith("-bwd") else KERNEL_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -71,7 +84,7 @@ def measured_traffic(workload, kernel):
     except (OSError, ValueError):
         return None
     rec = t.get(workload, {}).get(kernel)
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -91,33 +104,36 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": CALIB_BYTES, "reps": CALIB_REPS}))
 
 
-def _pmc(path, counter, name_part):
+def _pmc(path, counter, kname):
     import csv
+    import re
+    pat = re.compile(r"(^|[^A-Za-z0-9_])" + re.escape(kname) + r"($|[^A-Za-z0-9_])")
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+            if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"])]
     if not vals:
-        raise SystemExit(f"no {counter} rows for {name_part!r} in {path}")
+        raise SystemExit(f"no {counter} rows for {kname!r} in {path}")
     return sum(vals) / len(vals)
 
 
 def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv):
     """HBM bytes per launch of each library kernel from rocprofv3 --pmc runs (KiB per dispatch),
     each counter scaled by what it reads for the copy kernel of known size."""
-    f_cal = CALIB_BYTES / 1024 / _pmc(calib_fetch_csv, "FETCH_SIZE", "copyBuffer")
-    w_cal = CALIB_BYTES / 1024 / _pmc(calib_write_csv, "WRITE_SIZE", "copyBuffer")
+    f_cal = CALIB_BYTES / 1024 / _pmc(calib_fetch_csv, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    w_cal = CALIB_BYTES / 1024 / _pmc(calib_write_csv, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         t = {}
     rec = {}
-    for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step"):
+    for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_chunk_carry_rev",
+                  "s6_chunk_bwd", "s6_reduce_bc", "s6_reduce_params"):
         try:
             fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
         except SystemExit:
             continue
         rec[kname] = {"bytes_per_launch": round((fk * f_cal + wk * w_cal) * 1024),
-                      "fetch_kib_raw": fk, "write_kib_raw": wk, "source_hash": kernel_source_hash()}
+                      "fetch_kib_raw": fk, "write_kib_raw": wk, "source_hash": kernel_source_hash(workload)}
     t[workload] = rec
     t["_calibration"] = {"fetch_factor": round(f_cal, 4), "write_factor": round(w_cal, 4),
                          "copy_bytes": CALIB_BYTES}
@@ -219,6 +235,90 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bwd_algorithmic_bytes(batch, L, D, N=16, io_bytes=2):
+    """x, delta, z, dout read and dx, ddelta, dz written once; B, C read; dB, dC (fp32) written;
+    parameters read and their gradients written."""
+    return (7 * batch * L * D * io_bytes + 2 * batch * L * N * (io_bytes + 4) + 2 * D * (N + 2) * 4)
+
+
+def bench_bwd(args, k):
+    """ssm_scan_bwd on a whole-sequence workload: gradients with respect to every input."""
+    import torch
+    from selective_state_space_39_amd import binding, inputs
+    s = inputs.make_config(k)
+    batch, L, D, N = s.shape
+    io = s.io
+    go = inputs.make_grad_outputs(batch, L, D, N, io=io, seed=(39, k), with_dh_last=False)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if io == "bf16":
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    f32 = lambda a: torch.from_numpy(a).to(dev)
+    x, dl, z, B, C, dout = (to_dev(a) for a in (s.x, s.delta, s.z, s.B, s.C, go.dout))
+    A, Dk, bias = f32(s.A), f32(s.Dskip), f32(s.dt_bias)
+    io_code = binding.SSM_BF16 if io == "bf16" else binding.SSM_F32
+    nws = binding.bwd_workspace_bytes(batch, L, D, io_code, args.chunk_len)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    chunk_len, n_chunks = binding.bwd_plan(batch, L, D, io_code, args.chunk_len)
+    grads = binding.scan_bwd(x, dl, A, B, C, Dk, bias, dout, z=z, chunk_len=args.chunk_len, workspace=ws)
+
+    def step():
+        binding.scan_bwd(x, dl, A, B, C, Dk, bias, dout, z=z, chunk_len=args.chunk_len, workspace=ws, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms_per_step = timed(args.steps) / args.steps
+    binding.timing_collect()
+    binding.timing_enable(True, BWD_DOMINANT)
+    timed(args.steps)
+    binding.timing_enable(False)
+    launches, kms = binding.timing_collect()[BWD_DOMINANT]
+    avg_ms = kms / launches
+    binding.timing_enable(True)
+    ms_all = timed(args.steps) / args.steps
+    binding.timing_enable(False)
+    breakdown = binding.timing_collect()
+
+    E = batch * L * D
+    abytes = bwd_algorithmic_bytes(batch, L, D, N, 2 if io == "bf16" else 4)
+    hbm_gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    achieved = E * BWD_SLOTS_PER_ELEMENT * 2 / (avg_ms * 1e-3) / 1e12
+    kernels = {n: {"launches": c, "avg_ms": round(t / c, 5)} for n, (c, t) in breakdown.items()}
+    kernels["_note"] = (f"every kernel bracketed by events in a separate pass: {ms_all:.4f} ms per step "
+                        f"with the events, {ms_per_step:.4f} without")
+    out = {"metric": "selective-scan backward elements/s (B·L·D), 1 MI355X", "value": round(E / (ms_per_step * 1e-3), 1),
+           "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{args.workload} ssm_scan_bwd", "batch": batch, "L": L, "D": D, "N": N, "io": io,
+                      "state": "f32", "gated": True, "chunk_len": chunk_len, "n_chunks": n_chunks},
+           "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
+                   "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes},
+           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_VALU_TFLOPS, 2),
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_VALU_TFLOPS, 4),
+                        "traffic": measured_traffic(args.workload, BWD_DOMINANT), "kernel": BWD_DOMINANT,
+                        "avg_launch_ms": round(avg_ms, 5),
+                        "work": f"{BWD_SLOTS_PER_ELEMENT} fp32 VALU slots (= {2 * BWD_SLOTS_PER_ELEMENT} "
+                                f"FMA-equivalent flops) per element x {E} elements per launch"},
+           "kernels": kernels}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +353,8 @@ def main():
     k = WORKLOADS[args.workload]
     if k == 5:
         return bench_decode(args)
+    if args.workload.endswith("-bwd"):
+        return bench_bwd(args, k)
     s = inputs.make_config(k)
     batch, L, D, N = s.shape
     io = s.io

@@ -133,31 +133,50 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry_rev(S6BwdArgs a) {
 // sums of 16 per-lane values over the wavefront
 // ---------------------------------------------------------------------------
 // Reduce-scatter by halving: at each level a lane keeps one half of its
-// values, sends the other half to the lane that differs in one lane-index bit
-// and adds what it receives.  Afterwards lane l holds the wavefront sum of
-// value l >> 2 (the four lanes 4i..4i+3 hold the same sum).  Every value is
-// first scaled by `keep` (0 for lanes that only duplicate another channel).
-__device__ __forceinline__ float wave_sum16(float (&v)[16], float keep) {
+// values and adds the same half from a partner lane that differs in one
+// lane-index bit, while the partner keeps (and receives) the other half.
+// Lane distance 32 and 16 use the gfx950 half-swaps (one instruction moves a
+// pair of registers), distance 8 a DPP row rotation, and the last three lane
+// bits DPP mirrors and quad permutes inside rows.  Afterwards lane l holds the
+// wavefront sum of value l >> 2 (lanes 4i..4i+3 hold the same sum).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;         // lane i of a 16-lane row reads lane (i + 8) mod 16
+constexpr int kDppRowHalfMirror = 0x141;   // lane i of an 8-lane half row reads lane 7 - i
+constexpr int kDppQuadSwap2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadSwap1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+
+__device__ __forceinline__ float wave_sum16(float (&v)[16]) {
     const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    // distance 32: v[i] (kept by lanes 0-31) and v[i+8] (kept by lanes 32-63)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= keep;
-#pragma unroll
-    for (int lvl = 0; lvl < 4; ++lvl) {
-        const int k = 32 >> lvl;          // lane distance 32, 16, 8, 4
-        const int half = 8 >> lvl;        // values kept after this level
-        // bit-select on the values (a select between two array elements could
-        // otherwise become a per-lane register index)
-        const uint32_t m = (lane & k) ? 0xffffffffu : 0u;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + half]);
-            const float send = __uint_as_float((lo & m) | (hi & ~m));
-            const float kp = __uint_as_float((hi & m) | (lo & ~m));
-            v[i] = kp + __shfl_xor(send, k);
-        }
+    for (int i = 0; i < 8; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    const float s = v[0] + __shfl_xor(v[0], 2);
-    return s + __shfl_xor(s, 1);
+    // distance 16: rows 0 and 2 keep v[i], rows 1 and 3 keep v[i+4]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // distance 8 inside a row, then lane bit 2 via the half-row mirror
+    const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b3 ? v[i] : v[i + 2];
+        const float keep = b3 ? v[i + 2] : v[i];
+        v[i] = keep + dpp<kDppRowRor8>(send);
+    }
+    {
+        const float send = b2 ? v[0] : v[1];
+        const float keep = b2 ? v[1] : v[0];
+        v[0] = keep + dpp<kDppRowHalfMirror>(send);
+    }
+    const float s = v[0] + dpp<kDppQuadSwap2>(v[0]);
+    return s + dpp<kDppQuadSwap1>(s);
 }
 
 // A copy of a wave-uniform pointer that the compiler cannot prove equal to
@@ -273,14 +292,11 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
     const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
     float* pbc = a.part_bc + (g.row0 * G + g.group) * (2 * kN) + (lane >> 2);
 
-    for (int j = nsub - 1; j >= 0; --j) {
-        const int t0 = j * SUB;
-        if (j < nsub - 1) {
-#pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = ck[(static_cast<int64_t>(j) * kN + n) * D];
-        }
-        // loads of the sub-chunk's tokens (rows past the chunk end clamp to its last row)
-        typename LD::R rx[SUB], rd[SUB], rg[SUB], rz[SUB];
+    // Raw loads of a sub-chunk's tokens (rows past the chunk end clamp to its last
+    // row).  The next sub-chunk's loads, and its starting state, are issued
+    // before the current sub-chunk's adjoint pass, so they land meanwhile.
+    typename LD::R rx[SUB], rd[SUB], rg[SUB], rz[SUB];
+    auto issue = [&](int t0) {
 #pragma unroll
         for (int i = 0; i < SUB; ++i) {
             const uint32_t o = min(static_cast<uint32_t>(t0 + i) * rowb, last);
@@ -288,6 +304,15 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
             rd[i] = ld.load(DL, vo, o);
             rg[i] = ld.load(GO, vo, o);
             if (GATED) rz[i] = ld.load(Z, vo, o);
+        }
+    };
+    issue((nsub - 1) * SUB);
+    float hn[kN];
+    for (int j = nsub - 1; j >= 0; --j) {
+        const int t0 = j * SUB;
+        if (j < nsub - 1) {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) h[n] = hn[n];
         }
         // recompute: states before each token, step sizes, dy (and dz)
         float hs[SUB][kN];
@@ -334,6 +359,11 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
                 dys[i] = gv;
             }
         }
+        if (j > 0) {
+            issue(t0 - SUB);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) hn[n] = ck[(static_cast<int64_t>(j - 1) * kN + n) * D];
+        }
         // adjoint back through the sub-chunk
         {
             const T* Bs = opaque(Bc);
@@ -358,6 +388,9 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
                 float dt = dts[i];
                 asm volatile("" : "+v"(dt));     // recompute Abar here rather than keep 16 per token live
                 const float u = dt * xs[i];
+                // the dB / dC terms of lanes that only duplicate channel D-1 must add nothing
+                const float uk = g.active ? u : 0.0f;
+                const float dyk = g.active ? dy : 0.0f;
                 float du = 0.0f, sw = 0.0f;
                 float pb[kN], pc[kN];
 #pragma unroll
@@ -365,12 +398,12 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
                     const float ht = (i == SUB - 1) ? h[n] : hs[i + 1][n];
                     const float mu = fmaf(Cv.get(n), dy, rho[n]);
                     du = fmaf(mu, Bv.get(n), du);
-                    pc[n] = dy * ht;
+                    pc[n] = dyk * ht;
                     const float q = __builtin_amdgcn_exp2f(dt * A2[n]) * mu;
                     const float w = q * hs[i][n];
                     sw = fmaf(w, A2[n], sw);
                     dA[n] = fmaf(w, dt, dA[n]);
-                    pb[n] = mu * u;
+                    pb[n] = mu * uk;
                     rho[n] = q;
                 }
                 const float dxv = fmaf(du, dt, dy * Dd);
@@ -380,9 +413,8 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
                 store_io(DDL, vs, so, dv);
                 dD = fmaf(dy, xs[i], dD);
                 dbias += dv;
-                const float keep = g.active ? 1.0f : 0.0f;      // duplicate lanes add nothing
-                const float sb = wave_sum16(pb, keep);
-                const float sc = wave_sum16(pc, keep);
+                const float sb = wave_sum16(pb);
+                const float sc = wave_sum16(pc);
                 if ((lane & 3) == 0) {
                     float* q = pbc + static_cast<int64_t>(tt) * G * (2 * kN);
                     q[0] = sb;
@@ -421,18 +453,37 @@ __global__ __launch_bounds__(kBlock) void s6_reduce_bc(S6BwdArgs a) {
     else a.dC[row * kN + k - kN] = s;
 }
 
-// dA, dDskip, ddt_bias: one lane per (k, d); sums the batch x chunk partials.
+// dA, dDskip, ddt_bias: a workgroup per (64 channels, parameter k); its four
+// wavefronts sum every fourth (batch row, chunk) partial with eight
+// independent accumulators, then wavefront 0 adds the four sums in a fixed
+// order.
 __global__ __launch_bounds__(kBlock) void s6_reduce_params(S6BwdArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i >= kBwdParams * a.D) return;
-    const int64_t k = i / a.D, d = i % a.D;
+    __shared__ float part[kBlock / kWave][kWave];
+    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+    const int64_t k = blockIdx.y;
+    const int64_t dl = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    const int64_t d = dl < a.D ? dl : a.D - 1;
     const int64_t units = a.batch * a.n_chunks;
+    const int64_t stride = kBwdParams * a.D;
     const float* p = a.part_p + k * a.D + d;
-    float s = 0.0f;
-    for (int64_t u = 0; u < units; ++u) s += p[u * kBwdParams * a.D];
-    if (k < kN) a.dA[d * kN + k] = s;
-    else if (k == kN) a.dDskip[d] = s;
-    else a.ddt_bias[d] = s;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    int64_t u = wave;
+    for (; u + 7 * 4 < units; u += 8 * 4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += p[(u + 4 * j) * stride];
+    }
+    for (int j = 0; u < units; u += 4, ++j) acc[j & 7] += p[u * stride];
+    part[wave][lane] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    __syncthreads();
+    if (wave == 0 && dl < a.D) {
+        const float s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+        if (k < kN) a.dA[d * kN + k] = s;
+        else if (k == kN) a.dDskip[d] = s;
+        else a.ddt_bias[d] = s;
+    }
 }
 
 }  // namespace s6
@@ -471,10 +522,9 @@ static hipError_t launch_bwd_t(const S6BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(s6_reduce_bc, dim3(static_cast<unsigned>((nbc + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                        stream, a);
     s6_timing_mark("s6_reduce_bc", stream, false);
-    const int64_t np = kBwdParams * a.D;
     s6_timing_mark("s6_reduce_params", stream, true);
-    hipLaunchKernelGGL(s6_reduce_params, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       stream, a);
+    hipLaunchKernelGGL(s6_reduce_params, dim3(static_cast<unsigned>((a.D + kWave - 1) / kWave), kBwdParams),
+                       dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_reduce_params", stream, false);
     return hipGetLastError();
 }

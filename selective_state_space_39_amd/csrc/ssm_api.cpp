@@ -150,25 +150,44 @@ int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
     return SSM_OK;
 }
 
-// Backward plan: its dominant kernel holds three wavefronts per SIMD, so the
-// automatic chunk length aims at about four such wavefronts per SIMD in total.
+// Backward plan.  The per-chunk backward kernel holds two wavefronts per
+// SIMD, so it runs in rounds of 2048 wavefronts; the two carry passes hold
+// six.  Measured on the 130M-layer shape (bf16): ~2.2 us per token and round
+// for the backward kernel (64-token chunks: 3 rounds, 0.43 ms), and ~2.25 us
+// per token for both carry passes together at one round.  The plan takes
+// the chunk length (a multiple of 32) with the smallest estimate.
 struct BwdPlan {
     int64_t chunk_len, n_chunks;
     int64_t off_carry_S, off_carry_H, off_rcarry_S, off_rcarry_H, off_ckpt, off_bc, off_p;
     int64_t ws_bytes;
 };
 
-constexpr int64_t kBwdTargetWaves = 4 * kSimds;
+double est_bwd(int64_t batch, int64_t D, int64_t L, int64_t len) {
+    const int64_t groups = batch * ((D + 63) / 64);
+    const int64_t n = (L + len - 1) / len;
+    const double rounds = static_cast<double>((groups * n + 2 * kSimds - 1) / (2 * kSimds));
+    double t = 2.2 * rounds * static_cast<double>(len + 8);
+    if (n > 1) {
+        const double crounds = static_cast<double>((groups * (n - 1) + 6 * kSimds - 1) / (6 * kSimds));
+        t += 2.25 * crounds * static_cast<double>(len + 6) + 2.0 * (4.0 + 2.4e-5 * static_cast<double>(batch * D * (n - 1)));
+    }
+    return t;
+}
 
 int make_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, BwdPlan& p) {
     if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
         return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
                     (long long)chunk_len, (long long)kChunkAlign);
     if (chunk_len == 0) {
-        const int64_t groups = batch * ((D + 63) / 64);
-        const int64_t max_chunks = (L + kChunkAlign - 1) / kChunkAlign;
-        int64_t n = std::min(std::max<int64_t>((kBwdTargetWaves + groups - 1) / groups, 1), max_chunks);
-        chunk_len = ((L + n - 1) / n + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        const int64_t whole = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        int64_t best = whole;
+        double best_t = est_bwd(batch, D, L, whole);
+        for (int64_t len = whole - kChunkAlign; len >= kChunkAlign; len -= kChunkAlign) {
+            if ((L + len - 1) / len > kMaxGrid) break;
+            const double t = est_bwd(batch, D, L, len);
+            if (t < best_t * 0.999) { best_t = t; best = len; }
+        }
+        chunk_len = best;
     }
     p.chunk_len = chunk_len;
     p.n_chunks = (L + chunk_len - 1) / chunk_len;
