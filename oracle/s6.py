@@ -40,6 +40,16 @@ Training differentiates through the scan and the pages' own kernel recomputes
 the states for it instead of storing them ("DL0170 ...", point (3) and the
 paragraph after Figure 1); here they are simply stored.
 
+Local convolution.  conv_silu is the block's short local mixing step before
+the scan ("Mamba", "Block Structure": a local convolution adds short-range
+context; "Mamba: State Space Models", "What a Mamba Block Contains": a short
+convolution for local mixing).  The pages give neither its width nor an
+activation; the reading taken here is a causal depthwise convolution along
+time of width K <= 4 with a per-channel bias, followed by silu:
+x_t = silu(b_d + sum_k w_dk * xin_{t-K+1+k}), with the K-1 inputs before the
+sequence taken from conv_init (zeros when None).  conv_scan_fwd feeds its
+output to scan_fwd as x.
+
 Parity status: pinned.  The test suite checks this module against the
 Delta -> 0 pass-through, the LTI convolution (direct sum, FFT and geometric
 closed form), a brute-force causal-matrix sum ("Mamba", "Relation to
@@ -47,7 +57,9 @@ Mamba-2"), the overwrite limit ("DL0170 ...", point (2)), pure decay in
 closed form, sequence splitting and chained decode steps, and linearity; the
 backward against central finite differences of that brute-force sum, exact
 dot-product identities of the inputs in which the output is linear, the LTI
-transposed convolution, a one-token closed form and gradient splitting.
+transposed convolution, a one-token closed form and gradient splitting; the
+local convolution against numpy.convolve, scipy.signal.lfilter, impulse
+responses, causality and stream splitting through conv_init.
 """
 from __future__ import annotations
 
@@ -234,3 +246,41 @@ def scan_bwd(x, delta, A, B, C, Dskip, dt_bias, dout, z=None, h0=None, dh_last=N
     dv = dDelta * _sigmoid(v)                                             # softplus' = sigmoid
     return dict(x=dx, delta=dv, z=dz, A=dA, B=dB, C=dC,
                 Dskip=np.einsum("btd,btd->d", dy, x), dt_bias=dv.sum(axis=(0, 1)), h0=carry)
+
+
+# ---------------------------------------------------------------------------
+# the local convolution before the scan
+# ---------------------------------------------------------------------------
+
+def conv_silu(xin, w, b, conv_init=None, io: str = "f64"):
+    """silu of a causal depthwise convolution along time.
+
+    xin: (bt, L, D); w: (D, K) float32, tap k weighting xin_{t-K+1+k};
+    b: (D,); conv_init: (bt, K-1, D) inputs before the sequence, or None
+    (zeros), stored like xin.  Returns x (bt, L, D) float64.
+    """
+    if io != "f64":
+        xin = decode(xin, io)
+        conv_init = None if conv_init is None else decode(conv_init, io)
+    xin = np.asarray(xin, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    bt, L, D = xin.shape
+    K = w.shape[1]
+    head = np.zeros((bt, K - 1, D)) if conv_init is None else np.asarray(conv_init, dtype=np.float64)
+    padded = np.concatenate([head, xin], axis=1)                       # (bt, K-1+L, D)
+    v = np.broadcast_to(b, (bt, L, D)).copy()
+    for t in range(L):
+        for k in range(K):
+            v[:, t, :] += w[None, :, k] * padded[:, t + k, :]
+    return silu(v)
+
+
+def conv_scan_fwd(xin, conv_w, conv_b, delta, A, B, C, Dskip, dt_bias, z=None, h0=None, conv_init=None,
+                  io: str = "f64"):
+    """The scan fed by the local convolution: scan_fwd(conv_silu(xin), ...)."""
+    x = conv_silu(xin, conv_w, conv_b, conv_init, io=io)
+    if io != "f64":
+        delta, B, C = (decode(a, io) for a in (delta, B, C))
+        z = None if z is None else decode(z, io)
+    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)

@@ -1,7 +1,7 @@
 """Pins for the float64 oracle: results the pages and the mathematics fix.
 
 Each pin takes an oracle module ``m`` (exposing softplus, silu, recurrence,
-scan_fwd, state_update and scan_bwd) and raises AssertionError when ``m`` disagrees
+scan_fwd, state_update, scan_bwd, conv_silu and conv_scan_fwd) and raises AssertionError when ``m`` disagrees
 with a value that does not come from ``m`` itself. The same pins run against
 copies of the oracle with a planted mistake (tests/test_oracle_mutants.py),
 which must each fail at least one of them.
@@ -515,7 +515,95 @@ def pin_bwd_split(m):
         _close(ga["h0"], whole["h0"], 1e-12, f"split {L1} dh0")
 
 
+# ---------------------------------------------------------------------------
+# (i) the local convolution before the scan
+# ---------------------------------------------------------------------------
+
+def _silu_ref(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _conv_case(seed, bt=2, L=37, D=3, K=4, with_init=True):
+    r = _rng(seed)
+    return dict(xin=r.standard_normal((bt, L, D)), w=r.standard_normal((D, K)), b=r.standard_normal(D),
+                init=r.standard_normal((bt, K - 1, D)) if (with_init and K > 1) else None)
+
+
+def pin_conv_numpy_convolve(m):
+    """Pre-activation = bias + numpy.convolve of [init, xin] with the reversed taps ('valid' part)."""
+    for K in (1, 2, 3, 4):
+        c = _conv_case(30 + K, K=K, with_init=K > 1)
+        out = m.conv_silu(c["xin"], c["w"], c["b"], c["init"])
+        bt, L, D = c["xin"].shape
+        for bi in range(bt):
+            for d in range(D):
+                head = c["init"][bi, :, d] if c["init"] is not None else np.zeros(K - 1)
+                seq = np.concatenate([head, c["xin"][bi, :, d]])
+                v = c["b"][d] + np.convolve(seq, c["w"][d, ::-1], mode="valid")
+                _close(out[bi, :, d], _silu_ref(v), 1e-13, f"conv K={K} b={bi} d={d}")
+
+
+def pin_conv_lfilter(m):
+    """The same as an FIR filter (scipy.signal.lfilter) over [init, xin], first K-1 outputs dropped."""
+    c = _conv_case(35, K=4)
+    out = m.conv_silu(c["xin"], c["w"], c["b"], c["init"])
+    for bi in range(2):
+        for d in range(3):
+            seq = np.concatenate([c["init"][bi, :, d], c["xin"][bi, :, d]])
+            v = scipy.signal.lfilter(c["w"][d, ::-1], [1.0], seq)[3:] + c["b"][d]
+            _close(out[bi, :, d], _silu_ref(v), 1e-13, f"lfilter b={bi} d={d}")
+
+
+def pin_conv_impulse_and_causality(m):
+    """A unit impulse at t0 gives silu(w_{K-1-j}) at t0 + j, silu(0) = 0 elsewhere; later inputs
+    never change earlier outputs."""
+    K, L = 4, 20
+    w = _rng(36).standard_normal((1, K))
+    for t0 in (0, 5, L - 2):
+        xin = np.zeros((1, L, 1))
+        xin[0, t0, 0] = 1.0
+        out = m.conv_silu(xin, w, np.zeros(1))[0, :, 0]
+        ref = np.zeros(L)
+        for j in range(K):
+            if t0 + j < L:
+                ref[t0 + j] = _silu_ref(w[0, K - 1 - j])
+        _close(out, ref, 1e-15, f"impulse at {t0}")
+    c = _conv_case(37)
+    base = m.conv_silu(c["xin"], c["w"], c["b"], c["init"])
+    x2 = c["xin"].copy()
+    x2[:, 20:] += 5.0
+    moved = m.conv_silu(x2, c["w"], c["b"], c["init"])
+    assert np.array_equal(base[:, :20], moved[:, :20]), "an output depends on a later input"
+    assert not np.allclose(base[:, 20:23], moved[:, 20:23]), "the perturbed inputs must matter"
+
+
+def pin_conv_scan_split_and_identity(m):
+    """conv_scan over [0, L) = conv_scan over [L1, L) resumed from (h_L1, the last K-1 inputs);
+    identity taps (0, 0, 0, 1) with zero bias give scan_fwd(silu(xin))."""
+    c = _conv_case(38, L=40, D=3)
+    s = _random_case(39, L=40, D=3)
+    run = lambda sl, init, h0: m.conv_scan_fwd(c["xin"][:, sl], c["w"], c["b"], s["delta"][:, sl], s["A"],
+                                               s["B"][:, sl], s["C"][:, sl], s["Dskip"], s["dt_bias"],
+                                               z=s["z"][:, sl], h0=h0, conv_init=init)
+    full, hf = run(slice(None), c["init"], s["h0"])
+    for L1 in (3, 17, 39):
+        a, ha = run(slice(0, L1), c["init"], s["h0"])
+        tail = np.concatenate([c["init"], c["xin"][:, :L1]], axis=1)[:, -3:]
+        b, hb = run(slice(L1, None), tail, ha)
+        _close(np.concatenate([a, b], axis=1), full, 1e-13, f"conv scan split at {L1}")
+        _close(hb, hf, 1e-13, f"conv scan split state at {L1}")
+    w_id = np.zeros((3, 4))
+    w_id[:, 3] = 1.0
+    y1, h1 = m.conv_scan_fwd(c["xin"], w_id, np.zeros(3), s["delta"], s["A"], s["B"], s["C"], s["Dskip"],
+                             s["dt_bias"], z=s["z"], h0=s["h0"], conv_init=c["init"])
+    y2, h2 = m.scan_fwd(_silu_ref(c["xin"]), s["delta"], s["A"], s["B"], s["C"], s["Dskip"], s["dt_bias"],
+                        z=s["z"], h0=s["h0"])
+    _close(y1, y2, 1e-14, "identity taps")
+    _close(h1, h2, 1e-14, "identity taps state")
+
+
 PINS = [pin_softplus, pin_silu, pin_delta_zero_exact, pin_delta_tiny_bias, pin_lti_direct,
         pin_lti_fft, pin_lti_closed_form, pin_lti_lfilter, pin_brute_force, pin_overwrite,
         pin_pure_decay, pin_single_token, pin_split, pin_chained_steps, pin_linearity,
-        pin_bwd_finite_differences, pin_bwd_dot_products, pin_bwd_lti_transpose, pin_bwd_split]
+        pin_bwd_finite_differences, pin_bwd_dot_products, pin_bwd_lti_transpose, pin_bwd_split,
+        pin_conv_numpy_convolve, pin_conv_lfilter, pin_conv_impulse_and_causality, pin_conv_scan_split_and_identity]

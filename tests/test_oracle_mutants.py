@@ -74,6 +74,21 @@ MUTANTS = {
     "bwd-dDskip-uses-dout": ("Dskip=np.einsum(\"btd,btd->d\", dy, x)", "Dskip=np.einsum(\"btd,btd->d\", dout, x)"),
     "bwd-dbias-before-softplus-derivative": ("dt_bias=dv.sum(axis=(0, 1))", "dt_bias=dDelta.sum(axis=(0, 1))"),
     "bwd-dz-ungated-output": ("dz = dout * y * sg", "dz = dout * (y - Dskip * x) * sg"),
+    # the local convolution
+    "conv-taps-reversed": ("v[:, t, :] += w[None, :, k] * padded[:, t + k, :]",
+                           "v[:, t, :] += w[None, :, K - 1 - k] * padded[:, t + k, :]"),
+    "conv-window-shifted": ("v[:, t, :] += w[None, :, k] * padded[:, t + k, :]",
+                            "v[:, t, :] += w[None, :, k] * padded[:, min(t + k + 1, L + K - 2), :]"),
+    "conv-bias-dropped": ("v = np.broadcast_to(b, (bt, L, D)).copy()", "v = np.zeros((bt, L, D))"),
+    "conv-no-activation": ("    return silu(v)\n\n\ndef conv_scan_fwd", "    return v\n\n\ndef conv_scan_fwd"),
+    "conv-init-ignored": ("head = np.zeros((bt, K - 1, D)) if conv_init is None else np.asarray(conv_init, dtype=np.float64)",
+                          "head = np.zeros((bt, K - 1, D))"),
+    "conv-init-reversed": ("else np.asarray(conv_init, dtype=np.float64)",
+                           "else np.asarray(conv_init, dtype=np.float64)[:, ::-1]"),
+    "conv-scan-ignores-gate": ("    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)",
+                               "    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=None, h0=h0)"),
+    "conv-scan-ignores-h0": ("    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)",
+                             "    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=None)"),
 }
 
 
