@@ -126,6 +126,42 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z,
                  void* stream);
 
 /*
+ * The scan fed by the block's local convolution, fused: the scan input is
+ *
+ *     x_t = silu(conv_b_d + sum_{k<K} conv_w_dk * xin_{t-K+1+k})
+ *
+ * a causal depthwise convolution of width K = conv_k (1..4) along time,
+ * then silu, computed inside the scan kernels from xin, so x never goes
+ * through memory ("Mamba", "Block Structure": a local convolution adds
+ * short-range context before the selective SSM; "Mamba: State Space
+ * Models", "What a Mamba Block Contains": a short convolution for local
+ * mixing.  The pages give neither the width nor an activation: width <= 4
+ * and silu are the readings this library implements).  Everything else is
+ * ssm_scan_fwd with x replaced by the convolved input (Dskip multiplies the
+ * convolved x as well).
+ *
+ *   xin             (batch, L, D) io dtype, required.
+ *   conv_w          (D, conv_k) float32, tap k weighting xin_{t-K+1+k}; conv_b (D) float32.
+ *   conv_init       (batch, conv_k - 1, D) io dtype: the inputs just before the
+ *                   sequence (a stream continued), NULL = zeros.
+ *   conv_last       (batch, conv_k - 1, D) io dtype output: the last conv_k - 1
+ *                   inputs of [conv_init, xin], to pass as conv_init of the
+ *                   next segment; NULL = not wanted.
+ *   workspace       sized by ssm_scan_fwd_workspace_bytes for the same shape.
+ * Errors as ssm_scan_fwd; conv_k outside 1..4 is SSM_ERR_SHAPE.  conv_last
+ * must not overlap any input or other output.
+ */
+int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b, int64_t conv_k,
+                      const void* conv_init,
+                      const void* delta, const void* z, const void* B, const void* C,
+                      const float* A, const float* Dskip, const float* dt_bias,
+                      const float* h0,
+                      void* y, float* h_last, void* conv_last,
+                      int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                      int64_t chunk_len, void* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/*
  * Single-token decode step against a cached float32 state, in place.
  *
  * The recurrence advanced by one token ("Mamba & State-Space Sequence

@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_plan.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ssm_scan_fwd.restype = i32
     L.ssm_scan_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
+    L.ssm_conv_scan_fwd.restype = i32
+    L.ssm_conv_scan_fwd.argtypes = [vp, vp, vp, i64, vp] + [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     L.ssm_scan_bwd_plan.restype = i32
@@ -156,6 +158,56 @@ def scan_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, chunk_len: int = 0,
                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc)
     return y, h_last
+
+
+def conv_scan_fwd(xin, conv_w, conv_b, delta, A, B, C, D, dt_bias, z=None, h0=None, conv_init=None,
+                  chunk_len: int = 0, return_last_state: bool = True, return_conv_last: bool = False,
+                  out=None, workspace=None):
+    """The scan fed by the fused local convolution: x = silu(causal depthwise conv(xin) + conv_b).
+
+    conv_w: (D, K) float32 with K = 1..4; conv_b: (D,) float32; conv_init:
+    (batch, K-1, D) like xin or None.  Returns (y, h_last, conv_last) with
+    conv_last (batch, K-1, D) only when return_conv_last (else None).
+    """
+    if xin.dim() != 3:
+        raise ValueError("xin must be (batch, L, D)")
+    batch, L, Dc = xin.shape
+    dev = xin.device
+    io = _io(xin)
+    dt = xin.dtype
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be (D, K)")
+    K = conv_w.shape[1]
+    _need(conv_w, "conv_w", (Dc, K), torch.float32, dev)
+    _need(conv_b, "conv_b", (Dc,), torch.float32, dev)
+    for t, name in ((xin, "xin"), (delta, "delta")):
+        _need(t, name, (batch, L, Dc), dt, dev)
+    if z is not None:
+        _need(z, "z", (batch, L, Dc), dt, dev)
+    _need(B, "B", (batch, L, N_STATE), dt, dev)
+    _need(C, "C", (batch, L, N_STATE), dt, dev)
+    _need(A, "A", (Dc, N_STATE), torch.float32, dev)
+    _need(D, "D", (Dc,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (Dc,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, Dc, N_STATE), torch.float32, dev)
+    if conv_init is not None:
+        _need(conv_init, "conv_init", (batch, K - 1, Dc), dt, dev)
+    y = torch.empty_like(xin) if out is None else out
+    _need(y, "out", (batch, L, Dc), dt, dev)
+    h_last = torch.empty((batch, Dc, N_STATE), dtype=torch.float32, device=dev) if return_last_state else None
+    conv_last = torch.empty((batch, K - 1, Dc), dtype=dt, device=dev) if (return_conv_last and K > 1) else None
+    nws = workspace_bytes(batch, L, Dc, io, chunk_len)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nws:
+        raise ValueError(f"workspace too small: {nws} bytes needed")
+    rc = lib().ssm_conv_scan_fwd(_ptr(xin), _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_init), _ptr(delta), _ptr(z),
+                                 _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last),
+                                 _ptr(conv_last), batch, L, Dc, N_STATE, io, chunk_len, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return y, h_last, conv_last
 
 
 def bwd_workspace_bytes(batch: int, L: int, D: int, io_dtype: int = SSM_BF16, chunk_len: int = 0) -> int:

@@ -83,6 +83,12 @@ struct S6ScanArgs {
     int64_t chunk_len, n_chunks;
     int bf16;
     int pair_loads;    // bf16 with D even and x, delta, z 4-byte aligned: dword loads
+    // local convolution before the scan (conv_k = 0: none; x is then the scan input itself)
+    int conv_k;                    // width 1..4
+    const float* conv_w;           // (D, conv_k)
+    const float* conv_b;           // (D)
+    const void* conv_init;         // (batch, conv_k - 1, D) io inputs before the sequence, or NULL (zeros)
+    void* conv_last;               // (batch, conv_k - 1, D) io output: the last inputs, or NULL
 };
 
 struct S6StepArgs {

@@ -37,9 +37,66 @@
 namespace s6 {
 
 // ---------------------------------------------------------------------------
+// the local convolution before the scan (K = 0: none)
+// ---------------------------------------------------------------------------
+// x_t = silu(b_d + sum_k w_dk xin_{t-K+1+k}): a causal depthwise convolution of
+// width K along time, then silu.  Each lane keeps its channel's K-1 previous
+// inputs in registers, so the convolution reads every input once; a chunk
+// starts its window from the K-1 inputs before it (the previous chunk's last
+// tokens, or conv_init / zeros before the sequence).
+template <class IO, int K>
+struct ConvWin {
+    float w[K > 0 ? K : 1];
+    float bias;
+    float win[K > 1 ? K - 1 : 1];
+
+    __device__ __forceinline__ void init(const S6ScanArgs& a, const Geo& g) {
+        if constexpr (K > 0) {
+            using T = typename IO::T;
+#pragma unroll
+            for (int k = 0; k < K; ++k) w[k] = a.conv_w[g.d * K + k];
+            bias = a.conv_b[g.d];
+            const T* X = static_cast<const T*>(a.x);
+            const T* I = static_cast<const T*>(a.conv_init);
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                const int p = g.t0 - (K - 1) + i;                 // wave-uniform
+                if (p >= 0) win[i] = IO::load(X + (static_cast<int64_t>(g.b) * a.L + p) * a.D, g.d);
+                else if (I) win[i] = IO::load(I + (static_cast<int64_t>(g.b) * (K - 1) + (K - 1) + p) * a.D, g.d);
+                else win[i] = 0.0f;
+            }
+        }
+    }
+    // the convolved, activated input of the next token; shifts the window
+    __device__ __forceinline__ float apply(float xin) {
+        if constexpr (K == 0) {
+            return xin;
+        } else {
+            float v = bias;
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) v = fmaf(w[k], win[k], v);
+            v = fmaf(w[K - 1], xin, v);
+#pragma unroll
+            for (int k = 0; k + 1 < K - 1; ++k) win[k] = win[k + 1];
+            if constexpr (K > 1) win[K - 2] = xin;
+            return silu(v);
+        }
+    }
+    // the last K-1 inputs of the sequence, for a caller that continues the stream
+    __device__ __forceinline__ void store_last(const S6ScanArgs& a, const Geo& g) const {
+        if constexpr (K > 1) {
+            using T = typename IO::T;
+            T* O = static_cast<T*>(a.conv_last);
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) IO::store(O + (static_cast<int64_t>(g.b) * (K - 1) + i) * a.D, g.d, win[i]);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // phase 1: chunk carries
 // ---------------------------------------------------------------------------
-template <class LD>
+template <class LD, int K>
 __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
     using IO = typename LD::IO;
     using T = typename IO::T;
@@ -63,6 +120,8 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
     for (int n = 0; n < kN; ++n) { A2[n] = a.A[g.d * kN + n] * kLog2e; h[n] = 0.0f; }
     const float bias = a.dt_bias[g.d];
     float S = 0.0f;
+    ConvWin<IO, K> cv;
+    cv.init(a, g);
 
     st.issue(ld, src, vo, 0, rowb, last);
     st.widen(ld);
@@ -79,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
             const RowBC<IO>& Bv = bc[j & 1];
 
             const float dt = softplus(st.v[1][j] + bias);
-            const float dx = dt * st.v[0][j];
+            const float dx = dt * cv.apply(st.v[0][j]);
             S += dt;
 #pragma unroll
             for (int n = 0; n < kN; ++n) {
@@ -148,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) {
 // ---------------------------------------------------------------------------
 // phase 3: rescan from the starting state, write gated output (and h_L)
 // ---------------------------------------------------------------------------
-template <class LD, bool GATED>
+template <class LD, bool GATED, int K>
 __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
     using IO = typename LD::IO;
     using T = typename IO::T;
@@ -192,6 +251,8 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
     }
     const float bias = a.dt_bias[g.d];
     const float Dd = a.Dskip[g.d];
+    ConvWin<IO, K> cv;
+    cv.init(a, g);
 
     st.widen(ld);
     uint32_t so = 0;                 // row offset of the current token
@@ -211,7 +272,10 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
             const RowBC<IO>& Bv = bq[j & 1];
             const RowBC<IO>& Cv = cq[j & 1];
 
-            const float xv = st.v[0][j];
+            float xv = st.v[0][j];
+            if constexpr (K > 0) {
+                if (valid) xv = cv.apply(xv);                // masked tokens leave the window alone
+            }
             const float dt = valid ? softplus(st.v[1][j] + bias) : 0.0f;
             const float dx = dt * xv;
             float yv = Dd * xv;
@@ -226,6 +290,9 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
             so += rowb;
         }
         st.widen(ld);
+    }
+    if constexpr (K > 1) {
+        if (a.conv_last && g.c == a.n_chunks - 1) cv.store_last(a, g);
     }
     if (a.h_last && g.c == a.n_chunks - 1) {
 #pragma unroll
@@ -296,20 +363,20 @@ __global__ __launch_bounds__(kBlock) void s6_step(S6StepArgs a) {
 // ---------------------------------------------------------------------------
 using namespace s6;
 
-template <class LD, bool GATED>
+template <class LD, bool GATED, int K>
 static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
     const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
     if (a.n_chunks > 1) {
         dim3 g1(static_cast<unsigned>(nblk * (a.n_chunks - 1)));
         s6_timing_mark("s6_chunk_carry", stream, true);
-        hipLaunchKernelGGL(s6_chunk_carry<LD>, g1, dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((s6_chunk_carry<LD, K>), g1, dim3(kBlock), 0, stream, a);
         s6_timing_mark("s6_chunk_carry", stream, false);
         S6FoldArgs f{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0};
         s6_launch_fold(f, "s6_carry_scan", stream);
     }
     dim3 g3(static_cast<unsigned>(nblk * a.n_chunks));
     s6_timing_mark("s6_chunk_out", stream, true);
-    hipLaunchKernelGGL((s6_chunk_out<LD, GATED>), g3, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((s6_chunk_out<LD, GATED, K>), g3, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_chunk_out", stream, false);
     return hipGetLastError();
 }
@@ -325,18 +392,30 @@ void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
 void s6_launch_chunk_carry(const S6ScanArgs& a, hipStream_t stream) {
     dim3 g1(static_cast<unsigned>((a.D + kBlock - 1) / kBlock * a.batch * (a.n_chunks - 1)));
     s6_timing_mark("s6_chunk_carry", stream, true);
-    if (a.bf16 && a.pair_loads) hipLaunchKernelGGL(s6_chunk_carry<LdPairBF16>, g1, dim3(kBlock), 0, stream, a);
-    else if (a.bf16) hipLaunchKernelGGL(s6_chunk_carry<LdBF16>, g1, dim3(kBlock), 0, stream, a);
-    else hipLaunchKernelGGL(s6_chunk_carry<LdF32>, g1, dim3(kBlock), 0, stream, a);
+    if (a.bf16 && a.pair_loads) hipLaunchKernelGGL((s6_chunk_carry<LdPairBF16, 0>), g1, dim3(kBlock), 0, stream, a);
+    else if (a.bf16) hipLaunchKernelGGL((s6_chunk_carry<LdBF16, 0>), g1, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((s6_chunk_carry<LdF32, 0>), g1, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_chunk_carry", stream, false);
 }
 
-hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream) {
+template <int K>
+static hipError_t launch_scan_k(const S6ScanArgs& a, hipStream_t stream) {
     const bool gated = a.z != nullptr;
     if (a.bf16 && a.pair_loads)
-        return gated ? launch_scan_t<LdPairBF16, true>(a, stream) : launch_scan_t<LdPairBF16, false>(a, stream);
-    if (a.bf16) return gated ? launch_scan_t<LdBF16, true>(a, stream) : launch_scan_t<LdBF16, false>(a, stream);
-    return gated ? launch_scan_t<LdF32, true>(a, stream) : launch_scan_t<LdF32, false>(a, stream);
+        return gated ? launch_scan_t<LdPairBF16, true, K>(a, stream) : launch_scan_t<LdPairBF16, false, K>(a, stream);
+    if (a.bf16) return gated ? launch_scan_t<LdBF16, true, K>(a, stream) : launch_scan_t<LdBF16, false, K>(a, stream);
+    return gated ? launch_scan_t<LdF32, true, K>(a, stream) : launch_scan_t<LdF32, false, K>(a, stream);
+}
+
+hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream) {
+    switch (a.conv_k) {
+        case 0: return launch_scan_k<0>(a, stream);
+        case 1: return launch_scan_k<1>(a, stream);
+        case 2: return launch_scan_k<2>(a, stream);
+        case 3: return launch_scan_k<3>(a, stream);
+        case 4: return launch_scan_k<4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <class IO, bool GATED>

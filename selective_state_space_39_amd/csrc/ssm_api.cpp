@@ -337,11 +337,23 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dty
     return ok();
 }
 
-int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
-                 const float* A, const float* Dskip, const float* dt_bias, const float* h0,
-                 void* y, float* h_last,
-                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
-                 int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct ConvArgs {
+    int64_t k = 0;
+    const float* w = nullptr;
+    const float* b = nullptr;
+    const void* init = nullptr;
+    void* last = nullptr;
+};
+
+int scan_fwd_impl(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                  const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                  void* y, float* h_last, const ConvArgs& cv,
+                  int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                  int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
     int rc = check_shape(batch, L, D, N, io_dtype);
     if (rc) return rc;
     Plan p;
@@ -349,10 +361,16 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
     if (rc) return rc;
 
     struct { const void* p; const char* n; } req[] = {
-        {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
+        {x, cv.k ? "xin" : "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
         {dt_bias, "dt_bias"}, {y, "y"}};
     for (auto& r : req)
         if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    if (cv.k) {
+        if (cv.k < 1 || cv.k > 4) return fail(SSM_ERR_SHAPE, "conv_k = %lld: the local convolution has width 1 to 4",
+                                              (long long)cv.k);
+        if (!cv.w) return fail(SSM_ERR_NULL, "conv_w is NULL");
+        if (!cv.b) return fail(SSM_ERR_NULL, "conv_b is NULL");
+    }
     if (p.ws_bytes > 0) {
         if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)p.ws_bytes);
         if (workspace_bytes < p.ws_bytes)
@@ -364,21 +382,27 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
     struct { const void* p; int64_t a; const char* n; } al[] = {
         {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {B, 16, "B"}, {C, 16, "C"}, {y, es, "y"},
         {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 4, "h0"}, {h_last, 4, "h_last"},
-        {workspace, 16, "workspace"}};
+        {workspace, 16, "workspace"}, {cv.w, 4, "conv_w"}, {cv.b, 4, "conv_b"}, {cv.init, es, "conv_init"},
+        {cv.last, es, "conv_last"}};
     for (auto& r : al)
         if (r.p && !aligned(r.p, r.a))
             return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
 
     const int64_t seq = batch * L * D * es, bc = batch * L * kN * es, st = batch * D * kN * 4;
+    const int64_t win = cv.k > 1 ? batch * (cv.k - 1) * D * es : 0;
     const Range ins[] = {rng("x", x, seq), rng("delta", delta, seq), rng("z", z, seq), rng("B", B, bc),
                          rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
                          rng("dt_bias", dt_bias, D * 4), rng("h0", h0, st),
-                         rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes)};
-    const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st)};
+                         rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes),
+                         rng("conv_w", cv.w, D * cv.k * 4), rng("conv_b", cv.b, cv.k ? D * 4 : 0),
+                         rng("conv_init", cv.init, win)};
+    const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st), rng("conv_last", cv.last, win)};
     for (auto& o : outs)
         for (auto& i : ins)
             if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
-    if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
 
     S6ScanArgs a{};
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
@@ -393,9 +417,38 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
     a.chunk_len = p.chunk_len; a.n_chunks = p.n_chunks;
     a.bf16 = io_dtype == SSM_BF16;
     a.pair_loads = a.bf16 && D % 2 == 0 && aligned(x, 4) && aligned(delta, 4) && (!z || aligned(z, 4));
+    a.conv_k = static_cast<int>(cv.k);
+    a.conv_w = cv.w; a.conv_b = cv.b; a.conv_init = cv.init; a.conv_last = cv.last;
     hipError_t e = s6_launch_scan(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                 const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                 void* y, float* h_last,
+                 int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                 int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+    return scan_fwd_impl(x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last, ConvArgs{}, batch, L, D, N,
+                         io_dtype, chunk_len, workspace, workspace_bytes, stream);
+}
+
+int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b, int64_t conv_k,
+                      const void* conv_init, const void* delta, const void* z, const void* B, const void* C,
+                      const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                      void* y, float* h_last, void* conv_last,
+                      int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                      int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (conv_k < 1 || conv_k > 4)
+        return fail(SSM_ERR_SHAPE, "conv_k = %lld: the local convolution has width 1 to 4", (long long)conv_k);
+    ConvArgs cv;
+    cv.k = conv_k; cv.w = conv_w; cv.b = conv_b; cv.init = conv_init; cv.last = conv_last;
+    return scan_fwd_impl(xin, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last, cv, batch, L, D, N, io_dtype,
+                         chunk_len, workspace, workspace_bytes, stream);
 }
 
 int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,

@@ -225,6 +225,28 @@ def make_grad_outputs(batch: int, L: int, D: int, N: int = N_STATE, io: str = "b
     return GradOutputs(io=io, dout=_as_io(dout, io), dh_last=dh)
 
 
+@dataclass
+class ConvParams:
+    w: np.ndarray                     # (D, K) float32, tap k weighting xin_{t-K+1+k}
+    b: np.ndarray                     # (D,) float32
+    init: Optional[np.ndarray]        # (batch, K-1, D) io storage: inputs before the sequence, or None
+
+
+def make_conv_params(batch: int, D: int, K: int = 4, io: str = "bf16", seed=(SEED_ROOT, 0),
+                     with_init: bool = False) -> ConvParams:
+    """Local-convolution parameters from the stream (*seed, 3).
+
+    Draw order: w ~ U(-1/sqrt(K), 1/sqrt(K)) (D, K), b ~ N(0, 0.1^2) (D,),
+    init ~ N(0, 1) (batch, K-1, D) rounded to the io dtype.
+    """
+    rng = np.random.default_rng(list(seed) + [3] if not isinstance(seed, int) else [seed, 3])
+    lim = 1.0 / np.sqrt(K)
+    w = rng.uniform(-lim, lim, size=(D, K)).astype(np.float32)
+    b = _normal(rng, (D,), 0.1)
+    init = _as_io(_normal(rng, (batch, K - 1, D)), io) if (with_init and K > 1) else None
+    return ConvParams(w=w, b=b, init=init)
+
+
 def make_config(k: int) -> ScanInputs:
     """The whole-sequence workload number k (1..4), seeded with (39, k)."""
     c = CONFIGS[k]

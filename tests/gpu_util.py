@@ -120,3 +120,26 @@ def assert_grads_close(g, ref, tol, what, keys=GRAD_KEYS):
             assert g.get(k) is None, f"{what}: d{k} should be absent"
             continue
         assert_close(host64(g[k]), ref[k], tol, f"{what} d{k}")
+
+
+# ---------------------------------------------------------------------------
+# the scan fed by the local convolution
+# ---------------------------------------------------------------------------
+
+def gpu_conv_scan(s: inputs.ScanInputs, cp: inputs.ConvParams, chunk_len=0, h0=None, gated=True, conv_last=True):
+    io = s.io
+    y, h, cl = binding.conv_scan_fwd(dev(s.x, io), f32dev(cp.w), f32dev(cp.b), dev(s.delta, io), f32dev(s.A),
+                                     dev(s.B, io), dev(s.C, io), f32dev(s.Dskip), f32dev(s.dt_bias),
+                                     z=dev(s.z, io) if gated else None, h0=f32dev(h0),
+                                     conv_init=dev(cp.init, io), chunk_len=chunk_len, return_conv_last=conv_last)
+    torch.cuda.synchronize()
+    return y, h, cl
+
+
+def oracle_conv_scan(s: inputs.ScanInputs, cp: inputs.ConvParams, channels=None, h0=None, gated=True):
+    sel = slice(None) if channels is None else np.asarray(channels)
+    z = s.z[:, :, sel] if (gated and s.z is not None) else None
+    init = None if cp.init is None else cp.init[:, :, sel]
+    hh = None if h0 is None else h0[:, sel]
+    return oracle.conv_scan_fwd(s.x[:, :, sel], cp.w[sel], cp.b[sel], s.delta[:, :, sel], s.A[sel], s.B, s.C,
+                                s.Dskip[sel], s.dt_bias[sel], z=z, h0=hh, conv_init=init, io=s.io)

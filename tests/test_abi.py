@@ -234,3 +234,23 @@ def test_bwd_alignment(name, off):
 def test_bwd_alias(out, inp):
     f = FakeBwd()
     assert f.call(**{out: f.p[inp]}) == E_ALIAS
+
+
+def test_conv_scan_validation():
+    f = Fake()
+    v = ctypes.c_void_p
+    L = binding.lib()
+    p = f.p
+    base = 1 << 44
+    w, b, init, last = v(base), v(base + (1 << 24)), v(base + (2 << 24)), v(base + (3 << 24))
+
+    def call(k=4, conv_w=w, conv_b=b, conv_init=init, conv_last=last, y=p["y"], x=p["x"]):
+        return L.ssm_conv_scan_fwd(v(x), conv_w, conv_b, k, conv_init, v(p["delta"]), v(p["z"]), v(p["B"]),
+                                   v(p["C"]), v(p["A"]), v(p["Dskip"]), v(p["dt_bias"]), v(p["h0"]), v(y),
+                                   v(p["h_last"]), conv_last, f.batch, f.L, f.D, 16, f.io, 32, v(p["ws"]), 1 << 20,
+                                   None)
+    assert call(k=0) == E_SHAPE and call(k=5) == E_SHAPE
+    assert call(conv_w=None) == E_NULL and call(conv_b=None) == E_NULL
+    assert call(conv_init=v(base + (2 << 24) + 1)) == E_ALIGN
+    assert call(conv_last=v(p["x"])) == E_ALIAS             # conv_last on top of xin
+    assert call(conv_last=v(p["y"] + 64)) == E_ALIAS        # conv_last inside y

@@ -1,0 +1,79 @@
+"""The scan fed by the fused local convolution, on the GPU, against the float64 oracle (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, assert_close, dev, gpu_conv_scan, host64, log, oracle_conv_scan
+from selective_state_space_39_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("batch,L,D,io,K,gated,h0,init,chunk", [
+    (2, 300, 200, "bf16", 4, True, True, True, 64),     # 5 chunks, ragged tail, stream continued
+    (1, 257, 130, "f32", 3, False, False, False, 32),   # 9 chunks, last holds one token
+    (3, 97, 65, "bf16", 2, True, True, True, 32),       # odd D: 16-bit loads
+    (1, 64, 64, "f32", 1, True, False, False, 64),      # width 1: a per-channel scale, bias and silu
+    (1, 2, 16, "bf16", 4, True, False, True, 32),       # shorter than the window: conv_last keeps init rows
+    (4, 512, 320, "bf16", 4, True, True, True, 0),      # automatic plan
+])
+def test_conv_scan_matches_oracle(batch, L, D, io, K, gated, h0, init, chunk):
+    s = inputs.make_scan_inputs(batch, L, D, io=io, seed=(39, 5000 + L + D), gated=gated, with_h0=h0)
+    cp = inputs.make_conv_params(batch, D, K, io=io, seed=(39, 5000 + L + D), with_init=init)
+    log(f"conv scan {batch}x{L}x{D} {io} K={K} gated={gated} h0={h0} init={init} chunk {chunk}")
+    y, h, cl = gpu_conv_scan(s, cp, chunk_len=chunk, h0=s.h0, gated=gated)
+    ry, rh = oracle_conv_scan(s, cp, h0=s.h0, gated=gated)
+    assert_close(host64(y), ry, TOL[io], f"conv scan {batch}x{L}x{D} y")
+    assert_close(host64(h), rh, TOL[io], f"conv scan {batch}x{L}x{D} h_L")
+    if K > 1:
+        dec = (lambda a: oracle.decode(a, io))
+        head = dec(cp.init) if cp.init is not None else np.zeros((batch, K - 1, D))
+        ref_last = np.concatenate([head, dec(s.x)], axis=1)[:, -(K - 1):]
+        assert np.array_equal(host64(cl), ref_last), "conv_last must be the last K-1 inputs, bit for bit"
+    else:
+        assert cl is None
+
+
+def test_conv_scan_stream_split():
+    """conv_scan over [0, L) = conv_scan over [0, L1) then [L1, L) from (h_L1, conv_last)."""
+    io = "bf16"
+    s = inputs.make_scan_inputs(2, 500, 192, io=io, seed=(39, 5100), with_h0=True)
+    cp = inputs.make_conv_params(2, 192, 4, io=io, seed=(39, 5100), with_init=True)
+    d = {k: dev(getattr(s, k), io) for k in ("x", "delta", "z", "B", "C")}
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A, Dk, bias, w, b = f(s.A), f(s.Dskip), f(s.dt_bias), f(cp.w), f(cp.b)
+    run = lambda sl, h0, init: binding.conv_scan_fwd(d["x"][:, sl].contiguous(), w, b, d["delta"][:, sl].contiguous(),
+                                                     A, d["B"][:, sl].contiguous(), d["C"][:, sl].contiguous(), Dk,
+                                                     bias, z=d["z"][:, sl].contiguous(), h0=h0, conv_init=init,
+                                                     chunk_len=64, return_conv_last=True)
+    y, h, cl = run(slice(None), f(s.h0), dev(cp.init, io))
+    for L1 in (1, 64, 333):
+        ya, ha, ca = run(slice(0, L1), f(s.h0), dev(cp.init, io))
+        yb, hb, cb = run(slice(L1, None), ha, ca)
+        torch.cuda.synchronize()
+        assert_close(np.concatenate([host64(ya), host64(yb)], axis=1), host64(y), 1e-2, f"split {L1} y")
+        assert_close(host64(hb), host64(h), 1e-5, f"split {L1} h_L")
+        assert torch.equal(cb, cl)
+
+
+def test_conv_scan_full_size_sampled():
+    """The 130M-layer shape with a width-4 convolution, at the automatic plan, on 64 sampled channels."""
+    s = inputs.make_config(2)
+    cp = inputs.make_conv_params(8, 1536, 4, io="bf16", seed=(39, 2), with_init=False)
+    y, h, _ = gpu_conv_scan(s, cp, conv_last=False)
+    ch = np.random.default_rng([39, 5200]).choice(1536, size=64, replace=False)
+    ry, rh = oracle_conv_scan(s, cp, channels=ch)
+    assert_close(host64(y)[:, :, ch], ry, TOL["bf16"], "conv 130M layer y (sampled)")
+    assert_close(host64(h)[:, ch], rh, TOL["bf16"], "conv 130M layer h_L (sampled)")
+
+
+def test_conv_scan_errors():
+    s = inputs.make_scan_inputs(1, 64, 64, io="bf16", seed=(39, 5300))
+    x = dev(s.x, "bf16")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w5 = torch.zeros(64, 5, device="cuda")
+    with pytest.raises(binding.SSMError) as e:
+        binding.conv_scan_fwd(x, w5, f(np.zeros(64, np.float32)), x, f(s.A), dev(s.B, "bf16"), dev(s.C, "bf16"),
+                              f(s.Dskip), f(s.dt_bias))
+    assert e.value.status == -2
