@@ -284,3 +284,19 @@ def conv_scan_fwd(xin, conv_w, conv_b, delta, A, B, C, Dskip, dt_bias, z=None, h
         delta, B, C = (decode(a, io) for a in (delta, B, C))
         z = None if z is None else decode(z, io)
     return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)
+
+
+def conv_state_update(conv_state, h, xin, conv_w, conv_b, delta, A, B, C, Dskip, dt_bias, z=None,
+                      io: str = "f64"):
+    """One decode token through the local convolution and the scan.
+
+    conv_state: (bt, K-1, D) the last K-1 inputs (stored like xin); h: (bt, D, N);
+    xin, delta, z: (bt, D); B, C: (bt, N).  Returns (out (bt, D), h_new,
+    conv_state_new) where conv_state_new is [conv_state, xin] without its
+    oldest row; the inputs are not modified.
+    """
+    as_seq = lambda a: None if a is None else np.asarray(a)[:, None, :]
+    y, hn = conv_scan_fwd(as_seq(xin), conv_w, conv_b, as_seq(delta), A, as_seq(B), as_seq(C), Dskip, dt_bias,
+                          z=as_seq(z), h0=h, conv_init=conv_state, io=io)
+    both = np.concatenate([np.asarray(conv_state), np.asarray(xin)[:, None, :]], axis=1)
+    return y[:, 0, :], hn, both[:, 1:]

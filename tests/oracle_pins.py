@@ -602,8 +602,26 @@ def pin_conv_scan_split_and_identity(m):
     _close(h1, h2, 1e-14, "identity taps state")
 
 
+def pin_conv_chained_steps(m):
+    """Chained convolution decode steps (conv state of the last K-1 inputs) equal one conv scan."""
+    c = _conv_case(40, L=15, D=3)
+    s = _random_case(41, L=15, D=3)
+    full, hf = m.conv_scan_fwd(c["xin"], c["w"], c["b"], s["delta"], s["A"], s["B"], s["C"], s["Dskip"],
+                               s["dt_bias"], z=s["z"], h0=s["h0"], conv_init=c["init"])
+    cs, h = c["init"].copy(), s["h0"].copy()
+    for t in range(15):
+        before = cs.copy()
+        out, h, cs = m.conv_state_update(cs, h, c["xin"][:, t], c["w"], c["b"], s["delta"][:, t], s["A"],
+                                         s["B"][:, t], s["C"][:, t], s["Dskip"], s["dt_bias"], z=s["z"][:, t])
+        _close(out, full[:, t], 1e-13, f"conv decode step {t}")
+        assert np.array_equal(cs[:, :-1], before[:, 1:]) and np.array_equal(cs[:, -1], c["xin"][:, t]), \
+            "the conv state must shift by one input"
+    _close(h, hf, 1e-13, "conv decode chain final state")
+
+
 PINS = [pin_softplus, pin_silu, pin_delta_zero_exact, pin_delta_tiny_bias, pin_lti_direct,
         pin_lti_fft, pin_lti_closed_form, pin_lti_lfilter, pin_brute_force, pin_overwrite,
         pin_pure_decay, pin_single_token, pin_split, pin_chained_steps, pin_linearity,
         pin_bwd_finite_differences, pin_bwd_dot_products, pin_bwd_lti_transpose, pin_bwd_split,
-        pin_conv_numpy_convolve, pin_conv_lfilter, pin_conv_impulse_and_causality, pin_conv_scan_split_and_identity]
+        pin_conv_numpy_convolve, pin_conv_lfilter, pin_conv_impulse_and_causality, pin_conv_scan_split_and_identity,
+        pin_conv_chained_steps]

@@ -87,6 +87,8 @@ MUTANTS = {
                            "else np.asarray(conv_init, dtype=np.float64)[:, ::-1]"),
     "conv-scan-ignores-gate": ("    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)",
                                "    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=None, h0=h0)"),
+    "conv-decode-state-not-shifted": ("    return y[:, 0, :], hn, both[:, 1:]", "    return y[:, 0, :], hn, both[:, :-1]"),
+    "conv-decode-ignores-state": ("h0=h, conv_init=conv_state, io=io)", "h0=h, conv_init=None, io=io)"),
     "conv-scan-ignores-h0": ("    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=h0)",
                              "    return scan_fwd(x, delta, A, B, C, Dskip, dt_bias, z=z, h0=None)"),
 }
