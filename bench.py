@@ -45,7 +45,10 @@ PEAK_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12        # 78.64, fp32 vector witho
 SLOTS_PER_ELEMENT = 112
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
 WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5,
-             "mamba-130m-layer-bwd": 2, "mamba-2.8b-layer-bwd": 3}
+             "mamba-130m-layer-bwd": 2, "mamba-2.8b-layer-bwd": 3,
+             "mamba-130m-layer-conv": 2, "decode-256x5120-conv": 5}
+CONV_K = 4                          # width of the fused local convolution in the -conv workloads
+CONV_SLOTS = 10                     # per element: 4 FMA + silu (exp 2, rcp 2, add, mul)
 # Backward: algorithmic fp32 VALU issue slots per element (b, t, d), exp/log/rcp counted as 2:
 #   state recompute: softplus 7 + Delta*x 1 + 16 x (mul, exp, mul, fma) 80           = 88
 #   readout for the gate gradient: 16 FMA + skip                                       = 17
@@ -191,10 +194,19 @@ def bench_decode(args):
     y = torch.empty((batch, D), dtype=torch.bfloat16, device=dev)
     it = [0]
 
+    conv = args.workload.endswith("-conv")
+    if conv:
+        cp = inputs.make_conv_params(batch, D, CONV_K, io="bf16", seed=(39, 5), with_init=True)
+        cw, cb = f32(cp.w), f32(cp.b)
+        cstate = bf(cp.init)
+
     def step():
         x, dl, z, B, C = dtoks[it[0] & 7]
         it[0] += 1
-        binding.state_update(h, x, dl, tA, B, C, tD, tb, z=z, out=y)
+        if conv:
+            binding.conv_state_update(h, cstate, x, cw, cb, dl, tA, B, C, tD, tb, z=z, out=y)
+        else:
+            binding.state_update(h, x, dl, tA, B, C, tD, tb, z=z, out=y)
 
     for _ in range(args.warmup):
         step()
@@ -217,13 +229,14 @@ def bench_decode(args):
     binding.timing_enable(False)
     c, kms = binding.timing_collect()["s6_step"]
     avg_ms = kms / c
-    abytes = decode_bytes(batch, D)
+    abytes = decode_bytes(batch, D) + (2 * batch * (CONV_K - 1) * D * 2 + D * (CONV_K + 1) * 4 if conv else 0)
     achieved = abytes / (avg_ms * 1e-3) / 1e9
     out = {"metric": METRIC, "value": round(batch * D / (ms_per_step * 1e-3), 1), "unit": "elements/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": "decode-256x5120 ssm_state_update", "batch": batch, "D": D, "N": 16,
-                      "io": "bf16", "state": "f32", "gated": True},
+           "config": {"workload": f"{args.workload} {'ssm_conv_state_update' if conv else 'ssm_state_update'}",
+                      "batch": batch, "D": D, "N": 16, "io": "bf16", "state": "f32", "gated": True,
+                      **({"conv_k": CONV_K} if conv else {})},
            "hbm": {"achieved_gbps": round(abytes / (ms_per_step * 1e-3) / 1e9, 1), "peak_gbps": PEAK_HBM_GBPS,
                    "frac": round(abytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                    "algorithmic_bytes_per_step": abytes},
@@ -231,7 +244,8 @@ def bench_decode(args):
                         "frac": round(achieved / PEAK_HBM_GBPS, 4),
                         "traffic": measured_traffic(args.workload, "s6_step"), "kernel": "s6_step",
                         "avg_launch_ms": round(avg_ms, 5),
-                        "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters)"}}
+                        "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters"
+                                + (", + the conv state read and written" if conv else "") + ")"}}
     print(json.dumps(out), flush=True)
 
 
@@ -374,8 +388,17 @@ def main():
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     chunk_len, n_chunks = binding.plan(batch, L, D, io_code, args.chunk_len)
 
-    def step():
-        binding.scan_fwd(x, dl, A, B, C, Dk, bias, z=z, chunk_len=args.chunk_len, out=y, workspace=ws)
+    conv = args.workload.endswith("-conv")
+    if conv:
+        cp = inputs.make_conv_params(batch, D, CONV_K, io=io, seed=(39, k))
+        cw, cb = f32(cp.w), f32(cp.b)
+
+        def step():
+            binding.conv_scan_fwd(x, cw, cb, dl, A, B, C, Dk, bias, z=z, chunk_len=args.chunk_len, out=y,
+                                  workspace=ws)
+    else:
+        def step():
+            binding.scan_fwd(x, dl, A, B, C, Dk, bias, z=z, chunk_len=args.chunk_len, out=y, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -417,14 +440,15 @@ def main():
     dominant = DOMINANT
     launches, kms = kern[dominant]
     avg_ms = kms / launches
-    work_flops = E * SLOTS_PER_ELEMENT * 2          # one full pass of the method per launch
+    slots = SLOTS_PER_ELEMENT + (CONV_SLOTS if conv else 0)
+    work_flops = E * slots * 2                      # one full pass of the method per launch
     achieved = work_flops / (avg_ms * 1e-3) / 1e12
     traffic = measured_traffic(args.workload, dominant)
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_VALU_TFLOPS, 2),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_VALU_TFLOPS, 4), "traffic": traffic,
                 "kernel": dominant, "avg_launch_ms": round(avg_ms, 5),
-                "work": f"{SLOTS_PER_ELEMENT} fp32 VALU slots (= {2 * SLOTS_PER_ELEMENT} FMA-equivalent flops) "
-                        f"per element x {E} elements per launch"}
+                "work": f"{slots} fp32 VALU slots (= {2 * slots} FMA-equivalent flops) "
+                        f"per element x {E} elements per launch" + (" (incl. the width-4 convolution)" if conv else "")}
     kernels = {n: {"launches": c, "avg_ms": round(t / c, 5)} for n, (c, t) in breakdown.items()}
     kernels["_note"] = (f"every kernel bracketed by events in a separate pass: {ms_all:.4f} ms per step "
                         f"with the events, {ms_per_step:.4f} without")
@@ -433,12 +457,13 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic",
-           "config": {"workload": f"{args.workload} ssm_scan_fwd", "batch": batch, "L": L, "D": D, "N": N,
-                      "io": io, "state": "f32", "gated": True, "chunk_len": chunk_len, "n_chunks": n_chunks},
+           "config": {"workload": f"{args.workload} {'ssm_conv_scan_fwd' if conv else 'ssm_scan_fwd'}",
+                      "batch": batch, "L": L, "D": D, "N": N, "io": io, "state": "f32", "gated": True,
+                      "chunk_len": chunk_len, "n_chunks": n_chunks, **({"conv_k": CONV_K} if conv else {})},
            "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
                    "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes},
            "roofline": roofline, "kernels": kernels}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not conv:
         out["cpu_baseline"] = cpu_baseline(s)
     print(json.dumps(out), flush=True)
 

@@ -183,6 +183,24 @@ int ssm_state_update(float* h,
                      void* stream);
 
 /*
+ * Single-token decode step through the local convolution: the step input is
+ * silu(conv_b + conv_w . [conv_state, xin]) as in ssm_conv_scan_fwd, then
+ * ssm_state_update's step.  conv_state (batch, conv_k - 1, D) io dtype holds
+ * the last conv_k - 1 inputs and is shifted in place (oldest row dropped,
+ * xin appended); NULL allowed only for conv_k = 1.  Serving a stream: start
+ * from the conv_last and h_last of ssm_conv_scan_fwd over the prompt.  h,
+ * y and conv_state must not overlap each other or any input.
+ */
+int ssm_conv_state_update(float* h, void* conv_state,
+                          const void* xin, const float* conv_w, const float* conv_b, int64_t conv_k,
+                          const void* delta, const void* z,
+                          const void* B, const void* C,
+                          const float* A, const float* Dskip, const float* dt_bias,
+                          void* y,
+                          int64_t batch, int64_t D, int64_t N, int io_dtype,
+                          void* stream);
+
+/*
  * Workspace bytes and chunk plan of ssm_scan_bwd for this shape (the
  * backward always needs a workspace).  chunk_len as for ssm_scan_bwd.
  * Host-only; negative ssm_status for an invalid shape.

@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_conv_scan_fwd.restype = i32
     L.ssm_conv_scan_fwd.argtypes = [vp, vp, vp, i64, vp] + [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
+    L.ssm_conv_state_update.restype = i32
+    L.ssm_conv_state_update.argtypes = [vp] * 5 + [i64] + [vp] * 8 + [i64, i64, i64, i32, vp]
     L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     L.ssm_scan_bwd_plan.restype = i32
@@ -304,6 +306,40 @@ def state_update(h, x, delta, A, B, C, D, dt_bias, z=None, out=None):
     _need(y, "out", (batch, Dc), dt, dev)
     rc = lib().ssm_state_update(_ptr(h), _ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
                                 _ptr(dt_bias), _ptr(y), batch, Dc, N_STATE, io, _stream(dev))
+    _check(rc)
+    return y
+
+
+def conv_state_update(h, conv_state, xin, conv_w, conv_b, delta, A, B, C, D, dt_bias, z=None, out=None):
+    """One decode token through the local convolution: h (batch, D, 16) and conv_state
+    (batch, K-1, D) are updated in place; returns y (batch, D)."""
+    if xin.dim() != 2:
+        raise ValueError("xin must be (batch, D)")
+    batch, Dc = xin.shape
+    dev = xin.device
+    io = _io(xin)
+    dt = xin.dtype
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be (D, K)")
+    K = conv_w.shape[1]
+    _need(conv_w, "conv_w", (Dc, K), torch.float32, dev)
+    _need(conv_b, "conv_b", (Dc,), torch.float32, dev)
+    if K > 1:
+        _need(conv_state, "conv_state", (batch, K - 1, Dc), dt, dev)
+    _need(h, "h", (batch, Dc, N_STATE), torch.float32, dev)
+    _need(delta, "delta", (batch, Dc), dt, dev)
+    if z is not None:
+        _need(z, "z", (batch, Dc), dt, dev)
+    _need(B, "B", (batch, N_STATE), dt, dev)
+    _need(C, "C", (batch, N_STATE), dt, dev)
+    _need(A, "A", (Dc, N_STATE), torch.float32, dev)
+    _need(D, "D", (Dc,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (Dc,), torch.float32, dev)
+    y = torch.empty_like(xin) if out is None else out
+    _need(y, "out", (batch, Dc), dt, dev)
+    rc = lib().ssm_conv_state_update(_ptr(h), _ptr(conv_state if K > 1 else None), _ptr(xin), _ptr(conv_w),
+                                     _ptr(conv_b), K, _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+                                     _ptr(dt_bias), _ptr(y), batch, Dc, N_STATE, io, _stream(dev))
     _check(rc)
     return y
 

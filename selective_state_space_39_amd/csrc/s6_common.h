@@ -99,6 +99,11 @@ struct S6StepArgs {
     void* y;
     int64_t batch, D;
     int bf16;
+    // local convolution before the step (conv_k = 0: none; x is then the step input itself)
+    int conv_k;
+    const float* conv_w;           // (D, conv_k)
+    const float* conv_b;           // (D)
+    void* conv_state;              // (batch, conv_k - 1, D) io: the last inputs, shifted in place
 };
 
 struct S6BwdArgs {

@@ -307,7 +307,10 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
 // channel) are read and written as whole 16-byte vectors by consecutive lanes.
 constexpr int kStepRows = 8;      // batch rows per workgroup (A is loaded once for them)
 
-template <class IO, bool GATED>
+// With the local convolution (K > 0) the step input is silu(b + w . [conv
+// state, xin]); the four lanes of a channel compute it redundantly and the
+// first one shifts the conv state in place.
+template <class IO, bool GATED, int K>
 __global__ __launch_bounds__(kBlock) void s6_step(S6StepArgs a) {
     using T = typename IO::T;
     const int q = threadIdx.x & 3;
@@ -327,13 +330,36 @@ __global__ __launch_bounds__(kBlock) void s6_step(S6StepArgs a) {
     for (int j = 0; j < 4; ++j) A2[j] = a.A[d * kN + 4 * q + j] * kLog2e;
     const float bias = a.dt_bias[d];
     const float Dd = a.Dskip[d];
+    float cw[K > 0 ? K : 1], cb = 0.0f;
+    if constexpr (K > 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) cw[k] = a.conv_w[d * K + k];
+        cb = a.conv_b[d];
+    }
+    T* CS = static_cast<T*>(a.conv_state);
 
     const int64_t b_begin = static_cast<int64_t>(blockIdx.y) * kStepRows;
     const int64_t b_end = (b_begin + kStepRows < a.batch) ? b_begin + kStepRows : a.batch;
     for (int64_t b = b_begin; b < b_end; ++b) {
         const int64_t bd = b * a.D + d;
         const int64_t brow = b * a.D;
-        const float xv = IO::load(X + brow, dd);
+        float xv = IO::load(X + brow, dd);
+        if constexpr (K > 0) {
+            float win[K > 1 ? K - 1 : 1];
+            float v = cb;
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                win[i] = IO::load(CS + (b * (K - 1) + i) * a.D, dd);
+                v = fmaf(cw[i], win[i], v);
+            }
+            v = fmaf(cw[K - 1], xv, v);
+            if (active && q == 0) {
+#pragma unroll
+                for (int i = 0; i + 1 < K - 1; ++i) IO::store(CS + (b * (K - 1) + i) * a.D, dd, win[i + 1]);
+                if constexpr (K > 1) IO::store(CS + (b * (K - 1) + K - 2) * a.D, dd, xv);
+            }
+            xv = silu(v);
+        }
         const float dt = softplus(IO::load(DL + brow, dd) + bias);
         const float dx = dt * xv;
         float4* hp = reinterpret_cast<float4*>(a.h + bd * kN) + q;
@@ -418,18 +444,30 @@ hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream) {
     }
 }
 
-template <class IO, bool GATED>
+template <class IO, bool GATED, int K>
 static hipError_t launch_step_t(const S6StepArgs& a, hipStream_t stream) {
     dim3 g(static_cast<unsigned>((a.D + kBlock / 4 - 1) / (kBlock / 4)),
            static_cast<unsigned>((a.batch + kStepRows - 1) / kStepRows));
     s6_timing_mark("s6_step", stream, true);
-    hipLaunchKernelGGL((s6_step<IO, GATED>), g, dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((s6_step<IO, GATED, K>), g, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_step", stream, false);
     return hipGetLastError();
 }
 
-hipError_t s6_launch_step(const S6StepArgs& a, hipStream_t stream) {
+template <int K>
+static hipError_t launch_step_k(const S6StepArgs& a, hipStream_t stream) {
     const bool gated = a.z != nullptr;
-    if (a.bf16) return gated ? launch_step_t<BF16, true>(a, stream) : launch_step_t<BF16, false>(a, stream);
-    return gated ? launch_step_t<F32, true>(a, stream) : launch_step_t<F32, false>(a, stream);
+    if (a.bf16) return gated ? launch_step_t<BF16, true, K>(a, stream) : launch_step_t<BF16, false, K>(a, stream);
+    return gated ? launch_step_t<F32, true, K>(a, stream) : launch_step_t<F32, false, K>(a, stream);
+}
+
+hipError_t s6_launch_step(const S6StepArgs& a, hipStream_t stream) {
+    switch (a.conv_k) {
+        case 0: return launch_step_k<0>(a, stream);
+        case 1: return launch_step_k<1>(a, stream);
+        case 2: return launch_step_k<2>(a, stream);
+        case 3: return launch_step_k<3>(a, stream);
+        case 4: return launch_step_k<4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }

@@ -552,41 +552,79 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z, const void* B,
     return ok();
 }
 
-int ssm_state_update(float* h, const void* x, const void* delta, const void* z, const void* B, const void* C,
-                     const float* A, const float* Dskip, const float* dt_bias, void* y,
-                     int64_t batch, int64_t D, int64_t N, int io_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int state_update_impl(float* h, const void* x, const void* delta, const void* z, const void* B, const void* C,
+                      const float* A, const float* Dskip, const float* dt_bias, void* y,
+                      int64_t conv_k, const float* conv_w, const float* conv_b, void* conv_state,
+                      int64_t batch, int64_t D, int64_t N, int io_dtype, void* stream) {
     int rc = check_shape(batch, 1, D, N, io_dtype);
     if (rc) return rc;
     struct { const void* p; const char* n; } req[] = {
-        {h, "h"}, {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
+        {h, "h"}, {x, conv_k ? "xin" : "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
         {dt_bias, "dt_bias"}, {y, "y"}};
     for (auto& r : req)
         if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    if (conv_k) {
+        if (conv_k < 1 || conv_k > 4)
+            return fail(SSM_ERR_SHAPE, "conv_k = %lld: the local convolution has width 1 to 4", (long long)conv_k);
+        if (!conv_w) return fail(SSM_ERR_NULL, "conv_w is NULL");
+        if (!conv_b) return fail(SSM_ERR_NULL, "conv_b is NULL");
+        if (conv_k > 1 && !conv_state) return fail(SSM_ERR_NULL, "conv_state is NULL");
+    }
     const int64_t es = esize(io_dtype);
     struct { const void* p; int64_t a; const char* n; } al[] = {
         {h, 16, "h"}, {x, es, "x"}, {delta, es, "delta"}, {z, es, "z"}, {B, es, "B"}, {C, es, "C"},
-        {y, es, "y"}, {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}};
+        {y, es, "y"}, {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {conv_w, 4, "conv_w"},
+        {conv_b, 4, "conv_b"}, {conv_state, es, "conv_state"}};
     for (auto& r : al)
         if (r.p && !aligned(r.p, r.a))
             return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
     const int64_t tok = batch * D * es, bc = batch * kN * es, st = batch * D * kN * 4;
+    const int64_t cs = conv_k > 1 ? batch * (conv_k - 1) * D * es : 0;
     const Range ins[] = {rng("x", x, tok), rng("delta", delta, tok), rng("z", z, tok), rng("B", B, bc),
                          rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
-                         rng("dt_bias", dt_bias, D * 4)};
-    const Range hs = rng("h", h, st), ys = rng("y", y, tok);
-    for (auto& i : ins) {
-        if (overlap(hs, i)) return fail(SSM_ERR_ALIAS, "h overlaps %s", i.name);
-        if (overlap(ys, i)) return fail(SSM_ERR_ALIAS, "y overlaps %s", i.name);
-    }
-    if (overlap(hs, ys)) return fail(SSM_ERR_ALIAS, "y overlaps h");
+                         rng("dt_bias", dt_bias, D * 4), rng("conv_w", conv_w, D * conv_k * 4),
+                         rng("conv_b", conv_b, conv_k ? D * 4 : 0)};
+    const Range outs[] = {rng("h", h, st), rng("y", y, tok), rng("conv_state", conv_state, cs)};
+    for (auto& o : outs)
+        for (auto& i : ins)
+            if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
 
     S6StepArgs a{};
     a.h = h; a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
     a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y;
     a.batch = batch; a.D = D; a.bf16 = io_dtype == SSM_BF16;
+    a.conv_k = static_cast<int>(conv_k); a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_state;
     hipError_t e = s6_launch_step(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_state_update(float* h, const void* x, const void* delta, const void* z, const void* B, const void* C,
+                     const float* A, const float* Dskip, const float* dt_bias, void* y,
+                     int64_t batch, int64_t D, int64_t N, int io_dtype, void* stream) {
+    return state_update_impl(h, x, delta, z, B, C, A, Dskip, dt_bias, y, 0, nullptr, nullptr, nullptr, batch, D, N,
+                             io_dtype, stream);
+}
+
+int ssm_conv_state_update(float* h, void* conv_state, const void* xin, const float* conv_w, const float* conv_b,
+                          int64_t conv_k, const void* delta, const void* z, const void* B, const void* C,
+                          const float* A, const float* Dskip, const float* dt_bias, void* y,
+                          int64_t batch, int64_t D, int64_t N, int io_dtype, void* stream) {
+    if (conv_k < 1 || conv_k > 4)
+        return fail(SSM_ERR_SHAPE, "conv_k = %lld: the local convolution has width 1 to 4", (long long)conv_k);
+    return state_update_impl(h, xin, delta, z, B, C, A, Dskip, dt_bias, y, conv_k, conv_w, conv_b, conv_state,
+                             batch, D, N, io_dtype, stream);
 }
 
 }  // extern "C"

@@ -254,3 +254,20 @@ def test_conv_scan_validation():
     assert call(conv_init=v(base + (2 << 24) + 1)) == E_ALIGN
     assert call(conv_last=v(p["x"])) == E_ALIAS             # conv_last on top of xin
     assert call(conv_last=v(p["y"] + 64)) == E_ALIAS        # conv_last inside y
+
+
+def test_conv_decode_validation():
+    L = binding.lib()
+    v = ctypes.c_void_p
+    base = 1 << 40
+    p = [v(base + i * (1 << 24)) for i in range(13)]
+    # h, conv_state, xin, conv_w, conv_b | k | delta, z, B, C, A, Dskip, dt_bias, y
+    call = lambda q, k=4, N=16: L.ssm_conv_state_update(*q[:5], k, *q[5:], 4, 128, N, 1, None)
+    assert call(p, k=0) == E_SHAPE and call(p, k=5) == E_SHAPE
+    assert call(p, N=8) == E_N
+    q = list(p); q[1] = None
+    assert call(q) == E_NULL                      # conv state needed for K > 1
+    q = list(p); q[1] = p[0]
+    assert call(q) == E_ALIAS                     # conv state on top of h
+    q = list(p); q[1] = v(base + (1 << 24) + 1)
+    assert call(q) == E_ALIGN

@@ -77,3 +77,48 @@ def test_conv_scan_errors():
         binding.conv_scan_fwd(x, w5, f(np.zeros(64, np.float32)), x, f(s.A), dev(s.B, "bf16"), dev(s.C, "bf16"),
                               f(s.Dskip), f(s.dt_bias))
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("batch,D,io,K,gated", [(3, 130, "bf16", 4, True), (9, 64, "f32", 2, False),
+                                                 (17, 257, "bf16", 1, True), (1, 1, "bf16", 3, True)])
+def test_conv_decode_step_matches_oracle(batch, D, io, K, gated):
+    A, Dskip, dt_bias, h0 = inputs.decode_params(batch, D)
+    tok = inputs.decode_token(4, batch, D, io=io, gated=gated)
+    cp = inputs.make_conv_params(batch, D, K, io=io, seed=(39, 5400 + D), with_init=True)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    h = f(h0)
+    cs = dev(cp.init, io) if K > 1 else None
+    y = binding.conv_state_update(h, cs, dev(tok.x, io), f(cp.w), f(cp.b), dev(tok.delta, io), f(A), dev(tok.B, io),
+                                  dev(tok.C, io), f(Dskip), f(dt_bias), z=dev(tok.z, io) if gated else None)
+    torch.cuda.synchronize()
+    init = cp.init if K > 1 else np.zeros((batch, 0, D), dtype=tok.x.dtype)
+    ry, rh, rcs = oracle.conv_state_update(init, h0, tok.x, cp.w, cp.b, tok.delta, A, tok.B, tok.C, Dskip, dt_bias,
+                                           z=tok.z if gated else None, io=io)
+    assert_close(host64(y), ry, TOL[io], f"conv decode {batch}x{D} K={K} y")
+    assert_close(host64(h), rh, TOL[io], f"conv decode {batch}x{D} K={K} h")
+    if K > 1:
+        assert np.array_equal(host64(cs), oracle.decode(rcs, io)), "conv state must shift by one input exactly"
+
+
+def test_conv_prompt_then_decode_equals_scan():
+    """Serving a stream: conv scan over a prompt, then chained conv decode steps from its
+    (h_last, conv_last), equal the conv scan over the whole sequence (oracle)."""
+    io, batch, L, P, D = "bf16", 2, 120, 100, 96
+    s = inputs.make_scan_inputs(batch, L, D, io=io, seed=(39, 5500), with_h0=True)
+    cp = inputs.make_conv_params(batch, D, 4, io=io, seed=(39, 5500), with_init=True)
+    d = {k: dev(getattr(s, k), io) for k in ("x", "delta", "z", "B", "C")}
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A, Dk, bias, w, b = f(s.A), f(s.Dskip), f(s.dt_bias), f(cp.w), f(cp.b)
+    sl = lambda k: d[k][:, :P].contiguous()
+    _, h, cs = binding.conv_scan_fwd(sl("x"), w, b, sl("delta"), A, sl("B"), sl("C"), Dk, bias, z=sl("z"),
+                                     h0=f(s.h0), conv_init=dev(cp.init, io), chunk_len=32, return_conv_last=True)
+    outs = []
+    for t in range(P, L):
+        tk = lambda k: d[k][:, t].contiguous()
+        outs.append(binding.conv_state_update(h, cs, tk("x"), w, b, tk("delta"), A, tk("B"), tk("C"), Dk, bias,
+                                              z=tk("z")))
+    yd = torch.stack(outs, dim=1)
+    torch.cuda.synchronize()
+    ry, rh = oracle_conv_scan(s, cp, h0=s.h0)
+    assert_close(host64(yd), ry[:, P:], TOL[io], "prompt + decode y")
+    assert_close(host64(h), rh, TOL[io], "prompt + decode h")
