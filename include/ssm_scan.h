@@ -257,6 +257,37 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
                  void* stream);
 
 /*
+ * SSD (Mamba-2 style) layer: the selective SSM with a scalar decay per head.
+ *
+ * "Mamba", "Relation to Mamba-2" writes the layer as a causal matrix mixer
+ * and credits Mamba-2 with a faster chunk algorithm for it; "Mamba &
+ * State-Space Sequence Models", "Core mechanics" names the duality with a
+ * class of linear attention; "DL0170 Mamba Selective SSM vs Attention" has
+ * Mamba-2 raise N beyond 16.  The reading implemented: per head h (P = 64
+ * channels), Abar_t = exp(Delta_t,h * A_h) times the identity on the P x N
+ * state, Delta_t,h = softplus(delta_t,h + dt_bias_h), B_t and C_t shared by
+ * all heads,
+ *     h_t = Abar_t h_{t-1} + Delta_t,h x_t,h B_t^T,  y_t,h = h_t C_t + Dskip_h x_t,h,
+ * out = y * silu(z) when z is given.  Evaluated in chunks of 64 tokens with
+ * bf16 matrix-core products (fp32 accumulation, fp32 carried state).
+ *
+ *   x, z, y   (batch, L, H, 64) bf16; z NULL = ungated.  x 16-byte aligned.
+ *   delta     (batch, L, H) bf16.
+ *   B, C      (batch, L, N) bf16, N = 64 or 128, 16-byte aligned.
+ *   A, Dskip, dt_bias (H) float32.
+ *   h0, h_last (batch, H, 64, N) float32, 16-byte aligned; NULL = zeros / not wanted.
+ * io_dtype must be SSM_BF16 (SSM_ERR_DTYPE otherwise); N other than 64 or
+ * 128 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE.  No workspace.
+ */
+int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
+                const void* B, const void* C,
+                const float* A, const float* Dskip, const float* dt_bias,
+                const float* h0,
+                void* y, float* h_last,
+                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
+                void* stream);
+
+/*
  * Per-kernel timing, for measurement tools; not needed to compute anything.
  *
  * ssm_timing_enable(1, kernel) makes every later launch of the named kernel
@@ -266,7 +297,7 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  * kernels costs time, so time whole calls with recording off.  Kernel names:
  * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step", and for the
  * backward "s6_chunk_carry_rev", "s6_carry_scan_rev", "s6_chunk_bwd",
- * "s6_reduce_bc", "s6_reduce_params".  Returns SSM_OK.
+ * "s6_reduce_bc", "s6_reduce_params", and "ssd_chunked".  Returns SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the

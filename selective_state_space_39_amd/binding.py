@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_conv_scan_fwd.argtypes = [vp, vp, vp, i64, vp] + [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_conv_state_update.restype = i32
     L.ssm_conv_state_update.argtypes = [vp] * 5 + [i64] + [vp] * 8 + [i64, i64, i64, i32, vp]
+    L.ssm_ssd_fwd.restype = i32
+    L.ssm_ssd_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i64, i32, vp]
     L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     L.ssm_scan_bwd_plan.restype = i32
@@ -342,6 +344,39 @@ def conv_state_update(h, conv_state, xin, conv_w, conv_b, delta, A, B, C, D, dt_
                                      _ptr(dt_bias), _ptr(y), batch, Dc, N_STATE, io, _stream(dev))
     _check(rc)
     return y
+
+
+def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: bool = True, out=None):
+    """SSD (Mamba-2 style) layer with a scalar decay per head.
+
+    x, z: (batch, L, H, 64); delta: (batch, L, H); B, C: (batch, L, N) with N
+    = 64 or 128, all bfloat16; A, D, dt_bias: (H,) float32; h0: (batch, H,
+    64, N) float32.  Returns (y, h_last).
+    """
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, L, H, P)")
+    batch, L, H, P = x.shape
+    dev = x.device
+    io = _io(x)
+    dt = x.dtype
+    N = B.shape[-1]
+    _need(x, "x", (batch, L, H, P), dt, dev)
+    _need(delta, "delta", (batch, L, H), dt, dev)
+    if z is not None:
+        _need(z, "z", (batch, L, H, P), dt, dev)
+    _need(B, "B", (batch, L, N), dt, dev)
+    _need(C, "C", (batch, L, N), dt, dev)
+    for t, name in ((A, "A"), (D, "D"), (dt_bias, "dt_bias")):
+        _need(t, name, (H,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, H, P, N), torch.float32, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", (batch, L, H, P), dt, dev)
+    h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev) if return_last_state else None
+    rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
+                           _ptr(h0), _ptr(y), _ptr(h_last), batch, L, H, P, N, io, _stream(dev))
+    _check(rc)
+    return y, h_last
 
 
 def timing_enable(on: bool = True, kernel: Optional[str] = None) -> None:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm_scan.so")
-SOURCES = [os.path.join(CSRC, "s6_kernels.hip"), os.path.join(CSRC, "s6_bwd.hip"), os.path.join(CSRC, "ssm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "s6_kernels.hip"), os.path.join(CSRC, "s6_bwd.hip"), os.path.join(CSRC, "ssd_kernels.hip"),
+           os.path.join(CSRC, "ssm_api.cpp")]
 ARCH = "gfx950"
 
 # Packed FP32 (v_pk_fma_f32 and friends) stays off in every HIP file.
@@ -48,7 +49,7 @@ def build(asm_dir: str | None = None, quiet: bool = False) -> str:
             print(msg, file=sys.stderr)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
-        for src in SOURCES[:2]:
+        for src in SOURCES[:3]:
             out = os.path.join(asm_dir, os.path.basename(src).replace(".hip", ".s"))
             subprocess.run([hipcc(), *FLAGS, "--cuda-device-only", "-S", "-x", "hip", src, "-o", out],
                            check=True, capture_output=True)

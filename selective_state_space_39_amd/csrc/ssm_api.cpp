@@ -451,6 +451,49 @@ int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b,
                          chunk_len, workspace, workspace_bytes, stream);
 }
 
+int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                void* y, float* h_last,
+                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype, void* stream) {
+    if (io_dtype != SSM_BF16)
+        return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 io (its products run on bf16 matrix cores)");
+    if (N != 64 && N != 128) return fail(SSM_ERR_N, "N = %lld: the SSD layer is built for N = 64 or 128", (long long)N);
+    if (P != 64) return fail(SSM_ERR_SHAPE, "P = %lld: the SSD layer is built for 64 channels per head", (long long)P);
+    if (batch < 1 || L < 1 || H < 1)
+        return fail(SSM_ERR_SHAPE, "batch, L and H must be >= 1 (got %lld, %lld, %lld)", (long long)batch,
+                    (long long)L, (long long)H);
+    if (L > (int64_t(1) << 30) || H > (int64_t(1) << 20) || batch * H > (int64_t(1) << 31) - 1)
+        return fail(SSM_ERR_SHAPE, "shape too large");
+    const int64_t elems = mul_ck(mul_ck(mul_ck(batch, L), H), P);
+    if (elems < 0 || mul_ck(elems, 4) < 0) return fail(SSM_ERR_SHAPE, "batch * L * H * P overflows");
+    struct { const void* p; const char* n; } req[] = {
+        {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"}, {dt_bias, "dt_bias"}, {y, "y"}};
+    for (auto& r : req)
+        if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
+    struct { const void* p; int64_t a; const char* n; } al[] = {
+        {x, 16, "x"}, {z, 2, "z"}, {y, 2, "y"}, {delta, 2, "delta"}, {B, 16, "B"}, {C, 16, "C"},
+        {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 16, "h0"}, {h_last, 16, "h_last"}};
+    for (auto& r : al)
+        if (r.p && !aligned(r.p, r.a))
+            return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
+    const int64_t seq = elems * 2, st = batch * H * P * N * 4, bc = batch * L * N * 2;
+    const Range ins[] = {rng("x", x, seq), rng("delta", delta, batch * L * H * 2), rng("z", z, seq),
+                         rng("B", B, bc), rng("C", C, bc), rng("A", A, H * 4), rng("Dskip", Dskip, H * 4),
+                         rng("dt_bias", dt_bias, H * 4), rng("h0", h0, st)};
+    const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st)};
+    for (auto& o : outs)
+        for (auto& i : ins)
+            if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
+    if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+    SsdArgs a{};
+    a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias;
+    a.h0 = h0; a.y = y; a.h_last = h_last;
+    a.batch = batch; a.L = L; a.H = H; a.N = N;
+    hipError_t e = ssd_launch(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
                                      int64_t chunk_len) {
     int rc = check_shape(batch, L, D, N, io_dtype);

@@ -247,6 +247,52 @@ def make_conv_params(batch: int, D: int, K: int = 4, io: str = "bf16", seed=(SEE
     return ConvParams(w=w, b=b, init=init)
 
 
+@dataclass
+class SsdInputs:
+    io: str
+    x: np.ndarray                 # (batch, L, H, P) io storage
+    delta: np.ndarray             # (batch, L, H) io storage
+    z: Optional[np.ndarray]       # (batch, L, H, P) io storage
+    B: np.ndarray                 # (batch, L, N) io storage, shared by all heads
+    C: np.ndarray                 # (batch, L, N) io storage
+    A: np.ndarray                 # (H,) float32, negative
+    Dskip: np.ndarray             # (H,) float32
+    dt_bias: np.ndarray           # (H,) float32
+    h0: Optional[np.ndarray] = None   # (batch, H, P, N) float32
+
+    @property
+    def shape(self):
+        b, L, H, P = self.x.shape
+        return b, L, H, P, self.B.shape[-1]
+
+
+SSD_WORKLOAD = dict(name="mamba2-2.7b-layer", batch=8, L=2048, H=80, P=64, N=128, io="bf16")
+
+
+def make_ssd_inputs(batch: int, L: int, H: int, P: int = 64, N: int = 128, io: str = "bf16",
+                    seed=(SEED_ROOT, 6), gated: bool = True, with_h0: bool = False,
+                    delta_sigma: float = 0.5) -> SsdInputs:
+    """Seeded inputs for the SSD layer.
+
+    Draw order from ``numpy.random.default_rng(seed)``: A_h = -U(1, 16), u (->
+    dt_bias = softplus^-1 of a log-uniform step in [1e-3, 0.1]), x, delta, z,
+    B, C, h0.  x, z, B, C, h0 ~ N(0, 1); delta ~ N(0, delta_sigma^2); Dskip = 1.
+    """
+    rng = np.random.default_rng(list(seed) if not isinstance(seed, int) else seed)
+    A = (-rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    u = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), size=H))
+    dt_bias = inv_softplus(u).astype(np.float32)
+    x = _normal(rng, (batch, L, H, P))
+    dl = _normal(rng, (batch, L, H), delta_sigma)
+    z = _normal(rng, (batch, L, H, P)) if gated else None
+    B = _normal(rng, (batch, L, N))
+    C = _normal(rng, (batch, L, N))
+    h0 = _normal(rng, (batch, H, P, N)) if with_h0 else None
+    return SsdInputs(io=io, x=_as_io(x, io), delta=_as_io(dl, io), z=None if z is None else _as_io(z, io),
+                     B=_as_io(B, io), C=_as_io(C, io), A=A, Dskip=np.ones(H, dtype=np.float32), dt_bias=dt_bias,
+                     h0=h0)
+
+
 def make_config(k: int) -> ScanInputs:
     """The whole-sequence workload number k (1..4), seeded with (39, k)."""
     c = CONFIGS[k]

@@ -143,3 +143,24 @@ def oracle_conv_scan(s: inputs.ScanInputs, cp: inputs.ConvParams, channels=None,
     hh = None if h0 is None else h0[:, sel]
     return oracle.conv_scan_fwd(s.x[:, :, sel], cp.w[sel], cp.b[sel], s.delta[:, :, sel], s.A[sel], s.B, s.C,
                                 s.Dskip[sel], s.dt_bias[sel], z=z, h0=hh, conv_init=init, io=s.io)
+
+
+# ---------------------------------------------------------------------------
+# SSD layer
+# ---------------------------------------------------------------------------
+
+def gpu_ssd(s, gated=True, h0=True):
+    io = s.io
+    y, h = binding.ssd_fwd(dev(s.x, io), dev(s.delta, io), f32dev(s.A), dev(s.B, io), dev(s.C, io),
+                           f32dev(s.Dskip), f32dev(s.dt_bias), z=dev(s.z, io) if gated else None,
+                           h0=f32dev(s.h0) if h0 else None)
+    torch.cuda.synchronize()
+    return y, h
+
+
+def oracle_ssd(s, heads=None, gated=True, h0=True):
+    sel = slice(None) if heads is None else np.asarray(heads)
+    z = s.z[:, :, sel] if (gated and s.z is not None) else None
+    hh = s.h0[:, sel] if (h0 and s.h0 is not None) else None
+    return oracle.ssd_fwd(s.x[:, :, sel], s.delta[:, :, sel], s.A[sel], s.B, s.C, s.Dskip[sel], s.dt_bias[sel],
+                          z=z, h0=hh, io=s.io)

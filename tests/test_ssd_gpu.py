@@ -1,0 +1,67 @@
+"""The SSD (Mamba-2 style) layer on the GPU against the float64 oracle (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, assert_close, gpu_ssd, host64, log, oracle_ssd
+from selective_state_space_39_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("batch,L,H,N,gated,h0", [
+    (2, 200, 3, 128, True, True),      # 4 chunks, the last one 8 tokens
+    (1, 64, 2, 64, False, False),      # exactly one chunk
+    (1, 1, 1, 128, True, False),       # one token
+    (2, 1000, 4, 128, True, True),     # 16 chunks, ragged
+    (3, 130, 5, 64, True, True),       # N = 64, ragged
+])
+def test_ssd_matches_oracle(batch, L, H, N, gated, h0):
+    s = inputs.make_ssd_inputs(batch, L, H, N=N, seed=(39, 6000 + L + H), gated=gated, with_h0=h0)
+    log(f"ssd {batch}x{L}x{H}x64 N={N} gated={gated} h0={h0}")
+    y, h = gpu_ssd(s, gated=gated, h0=h0)
+    ry, rh = oracle_ssd(s, gated=gated, h0=h0)
+    assert_close(host64(y), ry, TOL["bf16"], f"ssd {batch}x{L}x{H} N={N} y")
+    assert_close(host64(h), rh, TOL["bf16"], f"ssd {batch}x{L}x{H} N={N} h_L")
+
+
+def test_ssd_split_resume():
+    s = inputs.make_ssd_inputs(2, 500, 3, seed=(39, 6100), with_h0=True)
+    y, h = gpu_ssd(s)
+    L1 = 201
+    cut = lambda a, sl: None if a is None else np.ascontiguousarray(a[:, sl])
+    a = inputs.SsdInputs(io=s.io, x=cut(s.x, slice(0, L1)), delta=cut(s.delta, slice(0, L1)),
+                         z=cut(s.z, slice(0, L1)), B=cut(s.B, slice(0, L1)), C=cut(s.C, slice(0, L1)),
+                         A=s.A, Dskip=s.Dskip, dt_bias=s.dt_bias, h0=s.h0)
+    ya, ha = gpu_ssd(a)
+    b = inputs.SsdInputs(io=s.io, x=cut(s.x, slice(L1, None)), delta=cut(s.delta, slice(L1, None)),
+                         z=cut(s.z, slice(L1, None)), B=cut(s.B, slice(L1, None)), C=cut(s.C, slice(L1, None)),
+                         A=s.A, Dskip=s.Dskip, dt_bias=s.dt_bias, h0=host64(ha).astype(np.float32))
+    yb, hb = gpu_ssd(b)
+    assert_close(np.concatenate([host64(ya), host64(yb)], axis=1), host64(y), TOL["bf16"], "ssd split y")
+    assert_close(host64(hb), host64(h), 1e-3, "ssd split h_L")
+
+
+def test_ssd_deterministic():
+    s = inputs.make_ssd_inputs(2, 300, 4, seed=(39, 6200), with_h0=True)
+    y1, h1 = gpu_ssd(s)
+    y2, h2 = gpu_ssd(s)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_ssd_full_size_sampled_heads():
+    """The 2.7B-layer workload (8 x 2048, 80 heads of 64, N = 128) on 3 sampled heads."""
+    w = inputs.SSD_WORKLOAD
+    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=(39, 6))
+    y, h = gpu_ssd(s, h0=False)
+    heads = [0, 41, 79]
+    ry, rh = oracle_ssd(s, heads=heads, h0=False)
+    assert_close(host64(y)[:, :, heads], ry, TOL["bf16"], "ssd 2.7B layer y (3 heads)")
+    assert_close(host64(h)[:, heads], rh, TOL["bf16"], "ssd 2.7B layer h_L (3 heads)")
+
+
+def test_ssd_errors():
+    s = inputs.make_ssd_inputs(1, 64, 2, N=96, seed=(39, 6300))
+    with pytest.raises(binding.SSMError) as e:
+        gpu_ssd(s)
+    assert e.value.status == -3
