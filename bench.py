@@ -46,7 +46,8 @@ SLOTS_PER_ELEMENT = 112
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
 WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5,
              "mamba-130m-layer-bwd": 2, "mamba-2.8b-layer-bwd": 3,
-             "mamba-130m-layer-conv": 2, "decode-256x5120-conv": 5}
+             "mamba-130m-layer-conv": 2, "decode-256x5120-conv": 5, "mamba2-2.7b-layer": 6}
+PEAK_BF16_TFLOPS = 2500.0           # dense bf16 matrix-core peak
 CONV_K = 4                          # width of the fused local convolution in the -conv workloads
 CONV_SLOTS = 10                     # per element: 4 FMA + silu (exp 2, rcp 2, add, mul)
 # Backward: algorithmic fp32 VALU issue slots per element (b, t, d), exp/log/rcp counted as 2:
@@ -62,6 +63,7 @@ KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/s6_kernels.hip",
                   "selective_state_space_39_amd/csrc/s6_device.h",
                   "selective_state_space_39_amd/csrc/s6_common.h"]
 BWD_KERNEL_SOURCES = KERNEL_SOURCES + ["selective_state_space_39_amd/csrc/s6_bwd.hip"]
+SSD_KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/ssd_kernels.hip", "selective_state_space_39_amd/csrc/s6_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -73,7 +75,9 @@ def algorithmic_bytes(batch, L, D, N=16, io_bytes=2):
 def kernel_source_hash(workload=""):
     """Hash of the sources the workload's kernels are compiled from."""
     h = hashlib.sha256()
-    for p in (BWD_KERNEL_SOURCES if workload.endswith("-bwd") else KERNEL_SOURCES):
+    srcs = (BWD_KERNEL_SOURCES if workload.endswith("-bwd") else
+            SSD_KERNEL_SOURCES if workload.startswith("mamba2") else KERNEL_SOURCES)
+    for p in srcs:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -130,7 +134,7 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
         t = {}
     rec = {}
     for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_chunk_carry_rev",
-                  "s6_chunk_bwd", "s6_reduce_bc", "s6_reduce_params"):
+                  "s6_chunk_bwd", "s6_reduce_bc", "s6_reduce_params", "ssd_chunked"):
         try:
             fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
         except SystemExit:
@@ -333,6 +337,76 @@ def bench_bwd(args, k):
     print(json.dumps(out), flush=True)
 
 
+def ssd_bytes(batch, L, H, P, N, gated=True):
+    """x read, y written (and z read) once; delta, B, C read; parameters read (bf16 io)."""
+    return (batch * L * H * P * 2 * (3 if gated else 2) + batch * L * H * 2 + 2 * batch * L * N * 2 + H * 12)
+
+
+def ssd_flops(batch, L, H, P, N, Q=64):
+    """Chunked evaluation: C B^T once per (batch row, chunk); per head and chunk the causal half of the
+    masked Q x Q x P product, the state term Q x N x P and the state update P x Q x N (2 flops per MAC)."""
+    chunks = -(-L // Q)
+    return batch * chunks * (2 * Q * Q * N + H * (Q * Q * P + 2 * Q * N * P + 2 * P * Q * N))
+
+
+def bench_ssd(args):
+    """The SSD (Mamba-2 style) layer on the 2.7B-layer shape: 8 x 2048 tokens, 80 heads of 64, N = 128."""
+    import torch
+    from selective_state_space_39_amd import binding, inputs
+    w = inputs.SSD_WORKLOAD
+    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=(39, 6))
+    batch, L, H, P, N = s.shape
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(a).to(dev)
+    x, dl, z, B, C = (bf(a) for a in (s.x, s.delta, s.z, s.B, s.C))
+    A, Dk, bias = f32(s.A), f32(s.Dskip), f32(s.dt_bias)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.ssd_fwd(x, dl, A, B, C, Dk, bias, z=z, out=y, return_last_state=False)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms_per_step = timed(args.steps) / args.steps
+    binding.timing_collect()
+    binding.timing_enable(True, "ssd_chunked")
+    timed(args.steps)
+    binding.timing_enable(False)
+    c, kms = binding.timing_collect()["ssd_chunked"]
+    avg_ms = kms / c
+    E = batch * L * H * P
+    abytes = ssd_bytes(batch, L, H, P, N)
+    flops = ssd_flops(batch, L, H, P, N)
+    gbps = abytes / (avg_ms * 1e-3) / 1e9
+    tflops = flops / (avg_ms * 1e-3) / 1e12
+    out = {"metric": "SSD layer elements/s (B·L·H·P), 1 MI355X", "value": round(E / (ms_per_step * 1e-3), 1),
+           "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "mamba2-2.7b-layer ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
+                      "io": "bf16", "state": "f32", "gated": True, "chunk": 64},
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, "ssd_chunked"),
+                        "kernel": "ssd_chunked", "avg_launch_ms": round(avg_ms, 5),
+                        "work": f"{abytes} algorithmic bytes per launch (x, z read, y written, delta, B, C)"},
+           "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": PEAK_BF16_TFLOPS,
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +439,8 @@ def main():
         sys.exit(1)
 
     k = WORKLOADS[args.workload]
+    if k == 6:
+        return bench_ssd(args)
     if k == 5:
         return bench_decode(args)
     if args.workload.endswith("-bwd"):

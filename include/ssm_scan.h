@@ -271,7 +271,7 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  * out = y * silu(z) when z is given.  Evaluated in chunks of 64 tokens with
  * bf16 matrix-core products (fp32 accumulation, fp32 carried state).
  *
- *   x, z, y   (batch, L, H, 64) bf16; z NULL = ungated.  x 16-byte aligned.
+ *   x, z, y   (batch, L, H, 64) bf16, 16-byte aligned; z NULL = ungated.
  *   delta     (batch, L, H) bf16.
  *   B, C      (batch, L, N) bf16, N = 64 or 128, 16-byte aligned.
  *   A, Dskip, dt_bias (H) float32.

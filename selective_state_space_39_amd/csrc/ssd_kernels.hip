@@ -23,6 +23,15 @@
 // accumulator tiles (G^T rows i = 4q .. 4q+3 of two 16-row tiles) are used
 // directly as the A operand of the y product, with the x operand read in the
 // same permuted k order.
+//
+// Operands whose contraction index runs along the rows of a row-major LDS
+// tile (B and the weighted x in the state update, x in the intra-chunk
+// product) are fetched with gfx950's transposing LDS read ds_read_b64_tr_b16:
+// within each 16-lane group, output lane j = 4a + c, element s comes from
+// the 8-byte segment addressed by lane 4s + a, element c.  Addressing lane
+// 4s + a at row (row0 + s), columns col0 + 4a .. 4a+3 therefore hands lane j
+// the column col0 + j of rows row0 .. row0+3 -- the k-major operand layout --
+// so no tile is ever stored transposed.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,6 +41,7 @@
 namespace ssd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;          // tokens per chunk
@@ -44,6 +54,14 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));      // round to nearest even
 }
 __device__ __forceinline__ float from_bf16(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) in one dword, low half first
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -52,117 +70,150 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {           // 16-byte aligned
     return *reinterpret_cast<const bf16x8*>(p);
 }
-__device__ __forceinline__ bf16x8 lds4x2(const uint16_t* p0, const uint16_t* p1) {   // two 8-byte halves
-    const uint2 a = *reinterpret_cast<const uint2*>(p0);
-    const uint2 b = *reinterpret_cast<const uint2*>(p1);
-    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
-    return __builtin_bit_cast(bf16x8, v);
-}
 __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
-    uint4 u;
-    u.x = to_bf16(v[0]) | (static_cast<uint32_t>(to_bf16(v[1])) << 16);
-    u.y = to_bf16(v[2]) | (static_cast<uint32_t>(to_bf16(v[3])) << 16);
-    u.z = to_bf16(v[4]) | (static_cast<uint32_t>(to_bf16(v[5])) << 16);
-    u.w = to_bf16(v[6]) | (static_cast<uint32_t>(to_bf16(v[7])) << 16);
-    return __builtin_bit_cast(bf16x8, u);
+    return __builtin_bit_cast(bf16x8, make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]),
+                                                 pack2(v[6], v[7])));
 }
 
 template <int N>
 struct alignas(16) Smem {
-    static constexpr int kLdN = N + 8;
-    uint16_t Bs[kQ][kLdN];      // B rows of the chunk          [i][n]
-    uint16_t Cs[kQ][kLdN];      // C rows of the chunk          [t][n]
-    uint16_t Bt[N][kLdQ];       // B transposed                 [n][i]
-    uint16_t Xt[kP][kLdQ];      // x transposed                 [p][i]
-    uint16_t XWt[kP][kLdQ];     // (exp(S_end - S_i) Delta_i x_i) transposed
-    uint16_t St[kP][kLdN];      // incoming state, bf16         [p][n]
+    static constexpr int kLdB = N + 24;   // 16-byte reads and transposing reads both conflict-free
+    static constexpr int kLdC = N + 24;
+    static constexpr int kLdX = kP + 16;
+    static constexpr int kLdM = kQ + 8;
+    uint16_t Bs[kQ][kLdB];      // B rows of the chunk          [i][n]
+    uint16_t Cs[kQ][kLdC];      // C rows of the chunk          [t][n]
+    uint16_t Xs[kQ][kLdX];      // x rows                       [i][p]
+    uint16_t XWs[kQ][kLdX];     // exp(S_end - S_i) Delta_i x_i [i][p]
+    uint16_t Ms[kQ][kLdM];      // masked mixer M[t][i] = (B_i . C_t) exp(S_t - S_i) Delta_i, i <= t
     float S2[kQ];               // S_t * log2(e)
     float Dl[kQ];               // Delta_t
 };
 
-// Global rows of one chunk, held in registers between chunks (prefetch).
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+// Transposing read: lane (group g = l / 16, local m = l % 16) addresses row
+// row0 + m / 4, columns col0 + 4 (m % 4); see the header comment.
+__device__ __forceinline__ v4s tr4(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+// k-major operand: lane l gets column col0 + l % 16 of rows row0 .. row0 + 7
+// (row0 may depend on the lane group)
+__device__ __forceinline__ bf16x8 opnd_rows8(const uint16_t* base, int ld, int row0, int col0) {
+    const int m = threadIdx.x & 15;
+    const uint16_t* p = base + (row0 + (m >> 2)) * ld + col0 + 4 * (m & 3);
+    const v4s lo = tr4(p), hi = tr4(p + 4 * ld);
+    return __builtin_bit_cast(bf16x8, static_cast<v8s>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+}
+// two 8-byte halves of one row: elements col0 .. col0+3 and col1 .. col1+3
+__device__ __forceinline__ bf16x8 lds4x2(const uint16_t* row, int col0, int col1) {
+    const uint2 a = *reinterpret_cast<const uint2*>(row + col0);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + col1);
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Every tensor of one (batch row, head) sequence is addressed through a buffer
+// resource based at its first element and bounded by its last row: a lane's
+// byte offset inside a chunk is fixed (a VGPR), the chunk's row offset is one
+// SGPR, and rows past the sequence end read as zero (stores there are
+// dropped), so no load or store needs a bounds check.
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+struct SeqIO {
+    __amdgpu_buffer_rsrc_t x, z, y, B, C, dl;
+    uint32_t xrow, bcrow, dlrow;             // bytes per token row
+};
+
+// Global data of one chunk, held in registers until it is staged (prefetch).
 template <int N>
 struct ChunkRegs {
     static constexpr int kXSeg = kQ * kP / 8 / kThreads;    // 16-byte pieces of x per thread
     static constexpr int kBSeg = kQ * N / 8 / kThreads;     // of B (and of C)
     uint4 x[kXSeg], b[kBSeg], c[kBSeg];
-    uint16_t dl;
+    uint16_t dl;               // delta of token (lane)
 };
 
 template <int N>
-__device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t b, int64_t h, int t0, int nt, ChunkRegs<N>& r) {
-    const int tid = threadIdx.x;
-    const uint16_t* X = static_cast<const uint16_t*>(a.x);
-    const uint16_t* Bg = static_cast<const uint16_t*>(a.B);
-    const uint16_t* Cg = static_cast<const uint16_t*>(a.C);
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ void load_chunk(const SeqIO& io, int t0, ChunkRegs<N>& r) {
+    const int tid = threadIdx.x, l = tid & 63;
+    const uint32_t so = static_cast<uint32_t>(t0);
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kXSeg; ++k) {
         const int s = tid + kThreads * k, t = s / (kP / 8), p0 = (s % (kP / 8)) * 8;
-        r.x[k] = t < nt ? *reinterpret_cast<const uint4*>(X + ((b * a.L + t0 + t) * a.H + h) * kP + p0) : zero;
+        r.x[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              io.x, t * io.xrow + p0 * 2, so * io.xrow, 0));
     }
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kBSeg; ++k) {
         const int s = tid + kThreads * k, t = s / (N / 8), n0 = (s % (N / 8)) * 8;
-        const int64_t row = (b * a.L + t0 + t) * N + n0;
-        r.b[k] = t < nt ? *reinterpret_cast<const uint4*>(Bg + row) : zero;
-        r.c[k] = t < nt ? *reinterpret_cast<const uint4*>(Cg + row) : zero;
+        r.b[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(io.B, t * io.bcrow + n0 * 2,
+                                                                                so * io.bcrow, 0));
+        r.c[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(io.C, t * io.bcrow + n0 * 2,
+                                                                                so * io.bcrow, 0));
     }
-    r.dl = 0;
-    if (tid < kQ && tid < nt) r.dl = static_cast<const uint16_t*>(a.delta)[(b * a.L + t0 + tid) * a.H + h];
+    r.dl = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(io.dl, l * io.dlrow, so * io.dlrow, 0));
 }
 
-// Stage one chunk into LDS: step sizes and the running log-decay S (wavefront
-// 0, a prefix sum over the 64 tokens), then B, C, x and the weighted x.
-template <int N>
-__device__ __forceinline__ void stage_chunk(Smem<N>& sm, const ChunkRegs<N>& r, int nt, float A, float bias) {
-    const int tid = threadIdx.x;
-    if (tid < kQ) {
-        const float dt = tid < nt ? s6::softplus(from_bf16(r.dl) + bias) : 0.0f;
-        float s = dt * A * kLog2e;
+// The gate at this lane's outputs: t = 16 tb + r, p = 16 w + 4 q .. +3 (8 bytes per t-block).
+__device__ __forceinline__ void load_gate(const SeqIO& io, int t0, int w, uint2 (&z)[4]) {
+    const int l = threadIdx.x & 63, rr = l & 15, q = l >> 4;
 #pragma unroll
-        for (int off = 1; off < kQ; off <<= 1) {                   // inclusive scan over the wavefront
-            const float o = __shfl_up(s, off);
-            if (tid >= off) s += o;
-        }
-        sm.S2[tid] = s;
-        sm.Dl[tid] = dt;
+    for (int tb = 0; tb < 4; ++tb)
+        z[tb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              io.z, (16 * tb + rr) * io.xrow + (16 * w + 4 * q) * 2,
+                                              static_cast<uint32_t>(t0) * io.xrow, 0));
+}
+
+// Stage one chunk into LDS.  Every wavefront scans the step sizes itself (lane
+// = token), so the weighted x needs no barrier: a lane takes S_t and Delta_t
+// of its rows from the scanning lanes.
+template <int N>
+__device__ __forceinline__ void stage_chunk(Smem<N>& sm, const ChunkRegs<N>& r, int nt, float A, float bias, int w) {
+    const int tid = threadIdx.x, l = tid & 63;
+    const float dt = l < nt ? s6::softplus(from_bf16(r.dl) + bias) : 0.0f;
+    float s = dt * A * kLog2e;
+#pragma unroll
+    for (int off = 1; off < kQ; off <<= 1) {                   // inclusive scan over the wavefront
+        const float o = __shfl_up(s, off);
+        if (l >= off) s += o;
     }
+    if (w == 0) {
+        sm.S2[l] = s;
+        sm.Dl[l] = dt;
+    }
+    const float s_end = __shfl(s, kQ - 1);
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kBSeg; ++k) {
-        const int s = tid + kThreads * k, t = s / (N / 8), n0 = (s % (N / 8)) * 8;
+        const int e = tid + kThreads * k, t = e / (N / 8), n0 = (e % (N / 8)) * 8;
         *reinterpret_cast<uint4*>(&sm.Bs[t][n0]) = r.b[k];
         *reinterpret_cast<uint4*>(&sm.Cs[t][n0]) = r.c[k];
-        const uint32_t w[4] = {r.b[k].x, r.b[k].y, r.b[k].z, r.b[k].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sm.Bt[n0 + j][t] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
     }
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kXSeg; ++k) {
-        const int s = tid + kThreads * k, t = s / (kP / 8), p0 = (s % (kP / 8)) * 8;
-        const uint32_t w[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+        const int e = tid + kThreads * k, t = e / (kP / 8), p0 = (e % (kP / 8)) * 8;
+        *reinterpret_cast<uint4*>(&sm.Xs[t][p0]) = r.x[k];
+        const float wt = __builtin_amdgcn_exp2f(s_end - __shfl(s, t)) * __shfl(dt, t);
+        const uint32_t w4[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+        uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.Xt[p0 + j][t] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+        for (int j = 0; j < 4; ++j) o[j] = pack2(wt * lo_bf16(w4[j]), wt * hi_bf16(w4[j]));
+        *reinterpret_cast<uint4*>(&sm.XWs[t][p0]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    __syncthreads();                                 // S2 and Dl ready
-    const float s_end = sm.S2[kQ - 1];
-#pragma unroll
-    for (int k = 0; k < ChunkRegs<N>::kXSeg; ++k) {
-        const int s = tid + kThreads * k, t = s / (kP / 8), p0 = (s % (kP / 8)) * 8;
-        const float wt = __builtin_amdgcn_exp2f(s_end - sm.S2[t]) * sm.Dl[t];
-        const uint32_t w[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float xv = from_bf16(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1))));
-            sm.XWt[p0 + j][t] = to_bf16(wt * xv);
-        }
-    }
+}
+
+// The ten 16 x 16 tiles (i-block, t-block) of the causal mixer, dealt to the
+// four wavefronts round-robin.
+__device__ __forceinline__ void tile_of(int k, int& ib, int& tb) {
+    tb = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+    ib = k - tb * (tb + 1) / 2;
 }
 
 template <int N, bool GATED>
-__global__ __launch_bounds__(kThreads) void ssd_chunked(SsdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
     constexpr int NB = N / 16;            // 16-row blocks of the state's n
-    constexpr int NBW = NB / 4;           // n-blocks of the state owned by each wavefront
     constexpr int KS = N / 32;            // k-steps of a product over n
     __shared__ Smem<N> sm;
 
@@ -176,139 +227,134 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked(SsdArgs a) {
     const int64_t b = u / a.H, h = u % a.H;
     const float A = a.A[h], bias = a.dt_bias[h], Dd = a.Dskip[h];
 
-    // state^T tiles owned by this wavefront: n-blocks w*NBW .. +NBW-1, p-blocks 0..3
-    f32x4 st[NBW][4];
+    // This wavefront owns channels p = 16 w .. 16 w + 15 of the state: tiles
+    // state^T[n-block nb][p-block w], lane slot i = state^T[16 nb + 4q + i][16 w + r].
+    f32x4 st[NB];
     const float* h0 = a.h0 ? a.h0 + (b * a.H + h) * kP * N : nullptr;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const int n = (w * NBW + nb) * 16 + 4 * q, p = pb * 16 + r;
-            if (h0) {
-                const float4 v = *reinterpret_cast<const float4*>(h0 + p * N + n);
-                st[nb][pb] = f32x4{v.x, v.y, v.z, v.w};
-            } else {
-                st[nb][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+    for (int nb = 0; nb < NB; ++nb) {
+        if (h0) {
+            const float4 v = *reinterpret_cast<const float4*>(h0 + (16 * w + r) * N + 16 * nb + 4 * q);
+            st[nb] = f32x4{v.x, v.y, v.z, v.w};
+        } else {
+            st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    auto write_state = [&]() {
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                const int n = (w * NBW + nb) * 16 + 4 * q, p = pb * 16 + r;
-                uint2 v;
-                v.x = to_bf16(st[nb][pb][0]) | (static_cast<uint32_t>(to_bf16(st[nb][pb][1])) << 16);
-                v.y = to_bf16(st[nb][pb][2]) | (static_cast<uint32_t>(to_bf16(st[nb][pb][3])) << 16);
-                *reinterpret_cast<uint2*>(&sm.St[p][n]) = v;
-            }
-    };
+    }
+    // the upper-triangle tiles of M that the y product reads are never written: zero them once
+    for (int e = tid; e < kQ * Smem<N>::kLdM; e += kThreads) (&sm.Ms[0][0])[e] = 0;
 
+    SeqIO io;
+    {
+        const int64_t xoff = (b * a.L * a.H + h) * kP;                       // first element of the sequence
+        const int64_t xbytes = ((a.L - 1) * a.H + 1) * kP * 2;
+        io.xrow = static_cast<uint32_t>(a.H * kP * 2);
+        io.bcrow = N * 2;
+        io.dlrow = static_cast<uint32_t>(a.H * 2);
+        io.x = rsrc(static_cast<const uint16_t*>(a.x) + xoff, xbytes);
+        io.z = rsrc(a.z ? static_cast<const uint16_t*>(a.z) + xoff : nullptr, a.z ? xbytes : 0);
+        io.y = rsrc(static_cast<uint16_t*>(a.y) + xoff, xbytes);
+        io.B = rsrc(static_cast<const uint16_t*>(a.B) + b * a.L * N, a.L * N * 2);
+        io.C = rsrc(static_cast<const uint16_t*>(a.C) + b * a.L * N, a.L * N * 2);
+        io.dl = rsrc(static_cast<const uint16_t*>(a.delta) + b * a.L * a.H + h, ((a.L - 1) * a.H + 1) * 2);
+    }
     const int nchunks = static_cast<int>((a.L + kQ - 1) / kQ);
     ChunkRegs<N> cr;
-    load_chunk<N>(a, b, h, 0, static_cast<int>(a.L < kQ ? a.L : kQ), cr);
-    write_state();
-    const uint16_t* Zg = static_cast<const uint16_t*>(a.z);
-    uint16_t* Yg = static_cast<uint16_t*>(a.y);
+    load_chunk<N>(io, 0, cr);
+    uint2 zc[4];
+    if constexpr (GATED) load_gate(io, 0, w, zc);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * kQ;
         const int nt = static_cast<int>(a.L - t0 < kQ ? a.L - t0 : kQ);
-        stage_chunk<N>(sm, cr, nt, A, bias);
+        __syncthreads();                               // previous chunk's LDS reads are done
+        stage_chunk<N>(sm, cr, nt, A, bias, w);
         __syncthreads();
-        if (c + 1 < nchunks) {
-            const int t1 = t0 + kQ;
-            load_chunk<N>(a, b, h, t1, static_cast<int>(a.L - t1 < kQ ? a.L - t1 : kQ), cr);
-        }
+        const int t1 = t0 + kQ;
+        if (c + 1 < nchunks) load_chunk<N>(io, t1, cr);
 
-        // --- G^T tiles (i-block ib, t-block w) for ib <= w, masked into M^T
-        f32x4 g[4];
+        // --- this wavefront's tiles of the masked mixer, into LDS
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            g[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (ib <= w) {
+        for (int slot = 0; slot < 3; ++slot) {
+            const int k = w + 4 * slot;
+            if (k < 10) {
+                int ib, tb;
+                tile_of(k, ib, tb);
+                f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    g[ib] = mfma(lds8(&sm.Bs[ib * 16 + r][ks * 32 + 8 * q]), lds8(&sm.Cs[w * 16 + r][ks * 32 + 8 * q]),
-                                 g[ib]);
-                const int t = w * 16 + r;
+                    g = mfma(lds8(&sm.Bs[ib * 16 + r][ks * 32 + 8 * q]), lds8(&sm.Cs[tb * 16 + r][ks * 32 + 8 * q]), g);
+                const int t = tb * 16 + r;
                 const float st2 = sm.S2[t];
+                float m4[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = ib * 16 + 4 * q + j;
                     const float m = __builtin_amdgcn_exp2f(st2 - sm.S2[i]) * sm.Dl[i];
-                    g[ib][j] = i <= t ? g[ib][j] * m : 0.0f;
+                    m4[j] = i <= t ? g[j] * m : 0.0f;
                 }
+                *reinterpret_cast<uint2*>(&sm.Ms[t][ib * 16 + 4 * q]) = make_uint2(pack2(m4[0], m4[1]),
+                                                                                    pack2(m4[2], m4[3]));
             }
         }
-        // --- y for t-block w: masked intra-chunk product plus the incoming state's term
-        f32x4 yd[4], yo[4];
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            yd[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            yo[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (2 * kb <= w) {
-                const float mv[8] = {g[2 * kb][0], g[2 * kb][1], g[2 * kb][2], g[2 * kb][3],
-                                     g[2 * kb + 1][0], g[2 * kb + 1][1], g[2 * kb + 1][2], g[2 * kb + 1][3]};
-                const bf16x8 am = pack8(mv);
-#pragma unroll
-                for (int pb = 0; pb < 4; ++pb) {
-                    const uint16_t* xr = &sm.Xt[pb * 16 + r][kb * 32 + 4 * q];
-                    yd[pb] = mfma(am, lds4x2(xr, xr + 16), yd[pb]);
-                }
-            }
-        }
+        // the incoming state as the bf16 A operand of the state term (m = p, k = n in the permuted order)
+        bf16x8 sa[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 ac = lds8(&sm.Cs[w * 16 + r][ks * 32 + 8 * q]);
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) yo[pb] = mfma(ac, lds8(&sm.St[pb * 16 + r][ks * 32 + 8 * q]), yo[pb]);
+            const float v8[8] = {st[2 * ks][0], st[2 * ks][1], st[2 * ks][2], st[2 * ks][3],
+                                 st[2 * ks + 1][0], st[2 * ks + 1][1], st[2 * ks + 1][2], st[2 * ks + 1][3]};
+            sa[ks] = pack8(v8);
         }
-        // --- outputs: rows t = 16w + 4q + j, column p = 16 pb + r
+        __syncthreads();                               // M complete
+
+        // --- y^T for this wavefront's 16 channels and every t-block:
+        //     lane slot j = y[t = 16 tb + r][p = 16 w + 4 q + j]
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = w * 16 + 4 * q + j;
-            if (t < nt) {
-                const float e = __builtin_amdgcn_exp2f(sm.S2[t]);
-                const int64_t row = ((b * a.L + t0 + t) * a.H + h) * kP;
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 yd = f32x4{0.f, 0.f, 0.f, 0.f}, yo = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) {
-                    const int p = pb * 16 + r;
-                    float yv = yd[pb][j] + e * yo[pb][j] + Dd * from_bf16(sm.Xt[p][t]);
-                    if (GATED) yv *= s6::silu(from_bf16(Zg[row + p]));
-                    Yg[row + p] = to_bf16(yv);
-                }
+            for (int kb = 0; kb <= tb / 2; ++kb)
+                yd = mfma(opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, kb * 32 + 8 * q, w * 16),
+                          lds8(&sm.Ms[tb * 16 + r][kb * 32 + 8 * q]), yd);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                yo = mfma(sa[ks], lds4x2(&sm.Cs[tb * 16 + r][0], ks * 32 + 4 * q, ks * 32 + 16 + 4 * q), yo);
+            // rows past the sequence end: stored through the bounded buffer, i.e. dropped
+            const int t = tb * 16 + r;
+            const float e = __builtin_amdgcn_exp2f(sm.S2[t]);
+            const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xs[t][w * 16 + 4 * q]);
+            float yv[4] = {yd[0] + e * yo[0] + Dd * lo_bf16(xv.x), yd[1] + e * yo[1] + Dd * hi_bf16(xv.x),
+                           yd[2] + e * yo[2] + Dd * lo_bf16(xv.y), yd[3] + e * yo[3] + Dd * hi_bf16(xv.y)};
+            if constexpr (GATED) {
+                yv[0] *= s6::silu(lo_bf16(zc[tb].x));
+                yv[1] *= s6::silu(hi_bf16(zc[tb].x));
+                yv[2] *= s6::silu(lo_bf16(zc[tb].y));
+                yv[3] *= s6::silu(hi_bf16(zc[tb].y));
             }
+            const uint2 o = make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, o), io.y, t * io.xrow + (w * 16 + 4 * q) * 2,
+                                                  static_cast<uint32_t>(t0) * io.xrow, 0);
+        }
+        if constexpr (GATED) {
+            if (c + 1 < nchunks) load_gate(io, t1, w, zc);
         }
         // --- state update: state^T = exp(S_end) state^T + B^T (w x)
         const float dec = __builtin_amdgcn_exp2f(sm.S2[kQ - 1]);
+        const bf16x8 xw0 = opnd_rows8(&sm.XWs[0][0], Smem<N>::kLdX, 8 * q, w * 16);
+        const bf16x8 xw1 = opnd_rows8(&sm.XWs[0][0], Smem<N>::kLdX, 32 + 8 * q, w * 16);
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                f32x4 s = st[nb][pb] * dec;
-#pragma unroll
-                for (int ks = 0; ks < kQ / 32; ++ks)
-                    s = mfma(lds8(&sm.Bt[(w * NBW + nb) * 16 + r][ks * 32 + 8 * q]),
-                             lds8(&sm.XWt[pb * 16 + r][ks * 32 + 8 * q]), s);
-                st[nb][pb] = s;
-            }
-        __syncthreads();                 // every wavefront is done with this chunk's LDS
-        write_state();
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4 sv = st[nb] * dec;
+            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw0, sv);
+            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw1, sv);
+            st[nb] = sv;
+        }
     }
     if (a.h_last) {
         float* hl = a.h_last + (b * a.H + h) * kP * N;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                const int n = (w * NBW + nb) * 16 + 4 * q, p = pb * 16 + r;
-                *reinterpret_cast<float4*>(hl + p * N + n) =
-                    make_float4(st[nb][pb][0], st[nb][pb][1], st[nb][pb][2], st[nb][pb][3]);
-            }
+        for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<float4*>(hl + (16 * w + r) * N + 16 * nb + 4 * q) =
+                make_float4(st[nb][0], st[nb][1], st[nb][2], st[nb][3]);
     }
 }
 

@@ -466,12 +466,15 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
         return fail(SSM_ERR_SHAPE, "shape too large");
     const int64_t elems = mul_ck(mul_ck(mul_ck(batch, L), H), P);
     if (elems < 0 || mul_ck(elems, 4) < 0) return fail(SSM_ERR_SHAPE, "batch * L * H * P overflows");
+    // one batch row's x (or y, z) and B, C are addressed with 32-bit byte offsets
+    if (L * H * P * 2 > (int64_t(1) << 31) - 1 || L * N * 2 > (int64_t(1) << 31) - 1)
+        return fail(SSM_ERR_SHAPE, "L * H * 64 * 2 bytes exceed 2 GiB per batch row");
     struct { const void* p; const char* n; } req[] = {
         {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"}, {dt_bias, "dt_bias"}, {y, "y"}};
     for (auto& r : req)
         if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
     struct { const void* p; int64_t a; const char* n; } al[] = {
-        {x, 16, "x"}, {z, 2, "z"}, {y, 2, "y"}, {delta, 2, "delta"}, {B, 16, "B"}, {C, 16, "C"},
+        {x, 16, "x"}, {z, 16, "z"}, {y, 16, "y"}, {delta, 2, "delta"}, {B, 16, "B"}, {C, 16, "C"},
         {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 16, "h0"}, {h_last, 16, "h_last"}};
     for (auto& r : al)
         if (r.p && !aligned(r.p, r.a))
