@@ -271,3 +271,24 @@ def test_conv_decode_validation():
     assert call(q) == E_ALIAS                     # conv state on top of h
     q = list(p); q[1] = v(base + (1 << 24) + 1)
     assert call(q) == E_ALIGN
+
+
+def test_ssd_validation():
+    L = binding.lib()
+    v = ctypes.c_void_p
+    base = 1 << 40
+    p = [v(base + i * (1 << 28)) for i in range(11)]
+    # x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last | batch, L, H, P, N, io
+    call = lambda q, P=64, N=128, io=1, H=4: L.ssm_ssd_fwd(*q, 2, 100, H, P, N, io, None)
+    assert call(p, io=0) == E_DTYPE                 # bf16 only
+    assert call(p, N=96) == E_N and call(p, N=16) == E_N
+    assert call(p, P=32) == E_SHAPE
+    assert call(p, H=0) == E_SHAPE
+    q = list(p); q[0] = None
+    assert call(q) == E_NULL
+    q = list(p); q[0] = v(base + 8)
+    assert call(q) == E_ALIGN                       # x must be 16-byte aligned
+    q = list(p); q[9] = p[0]
+    assert call(q) == E_ALIAS                       # y on top of x
+    q = list(p); q[10] = p[8]
+    assert call(q) == E_ALIAS                       # h_last on top of h0
