@@ -292,3 +292,20 @@ def test_ssd_validation():
     assert call(q) == E_ALIAS                       # y on top of x
     q = list(p); q[10] = p[8]
     assert call(q) == E_ALIAS                       # h_last on top of h0
+
+
+def test_last_error_is_per_thread():
+    """Each thread reads the message of its own last failing call."""
+    import threading
+    L = binding.lib()
+    out = {}
+
+    def worker(name, args):
+        for _ in range(200):
+            L.ssm_scan_fwd_workspace_bytes(*args)
+            out[name] = L.ssm_last_error().decode()
+
+    t1 = threading.Thread(target=worker, args=("n", (1, 10, 8, 8, 1, 0)))       # N != 16
+    t2 = threading.Thread(target=worker, args=("dtype", (1, 10, 8, 16, 7, 0)))  # bad dtype
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert "N = 8" in out["n"] and "dtype" in out["dtype"]

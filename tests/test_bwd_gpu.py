@@ -79,3 +79,20 @@ def test_bwd_errors_raise_before_launch():
     s, go = _case(1, 64, 64, "bf16", 4400)
     with pytest.raises(binding.SSMError):
         gpu_bwd(s, go, chunk_len=48)
+
+
+def test_bwd_outputs_overwrite_not_accumulate():
+    """Preallocated gradient buffers holding garbage (NaN) are overwritten: the result equals a fresh call."""
+    s, go = _case(2, 200, 96, "f32", 4500)
+    fresh = gpu_bwd(s, go, chunk_len=64)
+    shapes = {k: v for k, v in fresh.items() if v is not None}
+    junk = {k: torch.full_like(v, float("nan")) for k, v in shapes.items()}
+    from gpu_util import dev, f32dev
+    io = s.io
+    g = binding.scan_bwd(dev(s.x, io), dev(s.delta, io), f32dev(s.A), dev(s.B, io), dev(s.C, io),
+                         f32dev(s.Dskip), f32dev(s.dt_bias), dev(go.dout, io), z=dev(s.z, io), h0=f32dev(s.h0),
+                         dh_last=f32dev(go.dh_last), chunk_len=64, grads=junk)
+    torch.cuda.synchronize()
+    for k in shapes:
+        assert g[k].data_ptr() == junk[k].data_ptr()
+        assert torch.equal(g[k], fresh[k]), f"d{k} differs from a fresh call"

@@ -180,3 +180,31 @@ def test_errors_raise_before_launch():
     assert e.value.status == -7
     with pytest.raises(binding.SSMError):
         binding.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"], chunk_len=48)
+
+
+def test_nonfinite_inputs_propagate():
+    """A NaN in x reaches y at that token onward (through the state) and h_L; other rows stay finite."""
+    s = inputs.make_scan_inputs(2, 200, 64, io="f32", seed=(39, 2010))
+    s.x = s.x.copy()
+    s.x[0, 50, 3] = np.nan
+    y, h = gpu_scan(s, chunk_len=64)
+    yh, hh = host64(y), host64(h)
+    assert np.all(np.isfinite(yh[1])) and np.all(np.isfinite(hh[1])), "batch row 1 must stay finite"
+    assert np.all(np.isfinite(yh[0, :50])), "tokens before the NaN are unaffected"
+    assert np.isnan(yh[0, 50:, 3]).all(), "the NaN propagates through channel 3's state"
+    assert np.all(np.isfinite(np.delete(yh[0], 3, axis=1))), "other channels of row 0 stay finite"
+    assert np.isnan(hh[0, 3]).all()
+
+
+def test_side_stream():
+    """Calls enqueue on torch's current stream: a scan on a side stream matches the default-stream result."""
+    s = inputs.make_scan_inputs(2, 300, 130, io="bf16", seed=(39, 2011), with_h0=True)
+    t = _dev_all(s)
+    y0, h0 = _run(t, 64)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y1, h1 = binding.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"], z=t["z"],
+                                  h0=t["h0"], chunk_len=64)
+    side.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
