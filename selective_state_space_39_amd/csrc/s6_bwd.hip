@@ -17,13 +17,14 @@
 // state: a chunk scanned backward from mu = 0 leaves (S = sum Delta,
 // Lambda = Abar_{t0} mu_{t0}), and the incoming adjoint of chunk c-1 is
 // Lambda_c + exp(A S_c) * (incoming adjoint of chunk c).  Launch order:
-//   1. s6_chunk_carry + s6_carry_scan (the forward's): starting state per chunk;
+//   1. s6_chunk_ckpt: every chunk scanned from a zero state, storing the local
+//      state at each sub-chunk start and leaving the chunk carry;
+//      s6_carry_scan (the forward's fold): starting state per chunk;
 //   2. s6_chunk_carry_rev: adjoint carries of chunks 1..n-1;
 //      s6_carry_scan in reverse from dh_last: incoming adjoint per chunk;
-//   3. s6_chunk_bwd: per chunk, a forward sweep from the starting state stores
-//      the state at every kBwdSub-token sub-chunk start; then, sub-chunk by
-//      sub-chunk from the end, the states of the sub-chunk are recomputed into
-//      registers and the adjoint runs back through them;
+//   3. s6_chunk_bwd: per chunk, sub-chunk by sub-chunk from the end, the
+//      sub-chunk's starting state is rebuilt from its checkpoint, its states are
+//      recomputed into registers and the adjoint runs back through them;
 //   4. s6_reduce_bc / s6_reduce_params: deterministic sums of the per-wavefront
 //      dB, dC and per-chunk dA, dDskip, ddt_bias partials.
 
@@ -130,6 +131,79 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry_rev(S6BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// local states at every sub-chunk start (and the chunk carries)
+// ---------------------------------------------------------------------------
+// Every chunk (the last one too) is scanned from a zero state; before each
+// sub-chunk j >= 1 the local state and the step-size sum so far are stored
+// (17 values per lane), so that the backward pass gets the true state there
+// as local + exp(A * sum Delta) * (chunk starting state) instead of re-running
+// the chunk.  Chunks 0..n-2 also leave their carry for the state fold.
+template <class LD>
+__global__ __launch_bounds__(kBlock) void s6_chunk_ckpt(S6BwdArgs a) {
+    using IO = typename LD::IO;
+    using T = typename IO::T;
+    constexpr int NT = 2;
+    constexpr int SUB = kBwdSub;
+    static_assert(SUB % kBlk == 0, "a sub-chunk starts at a load block");
+    LD ld;
+    constexpr uint32_t es = sizeof(T);
+    Geo g;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks, 0, g)) return;
+    const uint32_t rowb = static_cast<uint32_t>(a.D) * es;
+    const uint32_t last = static_cast<uint32_t>(g.nt - 1) * rowb;
+    const int64_t e0 = g.row0 * a.D;
+    ChunkIO<IO> src[NT];
+    src[0].init(static_cast<const T*>(a.x) + e0, last + rowb);
+    src[1].init(static_cast<const T*>(a.delta) + e0, last + rowb);
+    const T* Bc = static_cast<const T*>(a.B) + g.row0 * kN;
+    const uint32_t vo = ld.voff(g.d);
+    const int64_t nsub_max = a.chunk_len / SUB;
+    float* ck = a.ckpt + ((static_cast<int64_t>(g.b) * a.n_chunks + g.c) * nsub_max * (kN + 1)) * a.D + g.d;
+    Stage<LD, NT> st;
+
+    float A2[kN], h[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { A2[n] = a.A[g.d * kN + n] * kLog2e; h[n] = 0.0f; }
+    const float bias = a.dt_bias[g.d];
+    float S = 0.0f;
+
+    st.issue(ld, src, vo, 0, rowb, last);
+    st.widen(ld);
+    RowBC<IO> bc[2];
+    bc[0].load(Bc);
+    for (int tb = 0; tb < g.nt; tb += kBlk) {
+        st.issue(ld, src, vo, static_cast<uint32_t>(tb + kBlk) * rowb, rowb, last);
+        if (tb > 0 && tb % SUB == 0) {                   // wave-uniform
+            float* p = ck + static_cast<int64_t>(tb / SUB) * (kN + 1) * a.D;
+#pragma unroll
+            for (int n = 0; n < kN; ++n) p[n * a.D] = h[n];
+            p[kN * a.D] = S;
+        }
+#pragma unroll
+        for (int j = 0; j < kBlk; ++j) {
+            const int tt = tb + j;
+            const bool valid = tt < g.nt;                 // wave-uniform
+            lgkm_wait_all();
+            bc[(j + 1) & 1].load(Bc + min(tt + 1, g.nt - 1) * kN);
+            const RowBC<IO>& Bv = bc[j & 1];
+            const float dt = valid ? softplus(st.v[1][j] + bias) : 0.0f;
+            const float dx = dt * st.v[0][j];
+            S += dt;
+#pragma unroll
+            for (int n = 0; n < kN; ++n)
+                h[n] = fmaf(__builtin_amdgcn_exp2f(dt * A2[n]), h[n], dx * Bv.get(n));
+        }
+        st.widen(ld);
+    }
+    if (g.c < a.n_chunks - 1) {
+        const int64_t cs = static_cast<int64_t>(g.b) * (a.n_chunks - 1) + g.c;
+        a.carry_S[cs * a.D + g.d] = S;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) a.carry_H[(cs * kN + n) * a.D + g.d] = h[n];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // sums of 16 per-lane values over the wavefront
 // ---------------------------------------------------------------------------
 // Reduce-scatter by halving: at each level a lane keeps one half of its
@@ -192,7 +266,7 @@ __device__ __forceinline__ P* opaque(P* p) {
 // per-chunk backward
 // ---------------------------------------------------------------------------
 template <class LD, bool GATED>
-__global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
+__global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
     using IO = typename LD::IO;
     using T = typename IO::T;
     constexpr int SUB = kBwdSub;
@@ -221,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
     const uint32_t vs = g.d * es;
     const int nsub = (g.nt + SUB - 1) / SUB;
     const int64_t nsub_max = a.chunk_len / SUB;
-    float* ck = a.ckpt + ((static_cast<int64_t>(g.b) * a.n_chunks + g.c) * nsub_max * kN) * D + g.d;
+    const float* ck = a.ckpt + ((static_cast<int64_t>(g.b) * a.n_chunks + g.c) * nsub_max * (kN + 1)) * D + g.d;
 
     float A2[kN], h[kN];
 #pragma unroll
@@ -241,36 +315,40 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
         for (int n = 0; n < kN; ++n) h[n] = 0.0f;
     }
 
-    // 1. forward sweep: the state at the start of every sub-chunk
-    {
-        const int sweep = (nsub - 1) * SUB;        // tokens before the last sub-chunk
-        const ChunkIO<IO> src[2] = {X, DL};
-        Stage<LD, 2> st;
-        st.issue(ld, src, vo, 0, rowb, last);
-        st.widen(ld);
-        RowBC<IO> bq[2];
-        bq[0].load(Bc);
-        for (int tb = 0; tb < sweep; tb += kBlk) {
-            st.issue(ld, src, vo, static_cast<uint32_t>(tb + kBlk) * rowb, rowb, last);
+    // The true state at the start of sub-chunk j >= 1 is its local state (from a
+    // zero state at the chunk start) plus the chunk's starting state decayed
+    // by exp(A * sum Delta) over the sub-chunks before it.  The chunk's starting
+    // state waits in LDS (four values per 16-byte slot, lanes contiguous).
+    __shared__ float4 hst_lds[kBlock / kWave][kN / 4][kWave];
+    const int wv = static_cast<int>(threadIdx.x) >> 6, ln = static_cast<int>(threadIdx.x) & (kWave - 1);
 #pragma unroll
-            for (int j = 0; j < kBlk; ++j) {
-                const int tt = tb + j;
-                if (tt % SUB == 0) {
+    for (int k = 0; k < kN / 4; ++k) hst_lds[wv][k][ln] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+    // Checkpoint j's 17 values are loaded one sub-chunk ahead (raw) and combined
+    // with the starting state only when needed, so the load latency is hidden.
+    auto ck_load = [&](int j, float (&loc)[kN], float& sl) {
+        const float* p = ck + static_cast<int64_t>(j) * (kN + 1) * D;
 #pragma unroll
-                    for (int n = 0; n < kN; ++n) ck[(static_cast<int64_t>(tt / SUB) * kN + n) * D] = h[n];
-                }
-                lgkm_wait_all();
-                bq[(j + 1) & 1].load(Bc + min(tt + 1, g.nt - 1) * kN);
-                const RowBC<IO>& Bv = bq[j & 1];
-                const float dt = softplus(st.v[1][j] + bias);
-                const float dx = dt * st.v[0][j];
+        for (int n = 0; n < kN; ++n) loc[n] = p[n * D];
+        sl = p[kN * D];
+    };
+    auto ck_combine = [&](int j, const float (&loc)[kN], float sl, float (&out)[kN]) {
 #pragma unroll
-                for (int n = 0; n < kN; ++n)
-                    h[n] = fmaf(__builtin_amdgcn_exp2f(dt * A2[n]), h[n], dx * Bv.get(n));
+        for (int k = 0; k < kN / 4; ++k) {
+            const float4 v = hst_lds[wv][k][ln];          // written by this lane: no barrier needed
+            const float hs0[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 4 * k + i;
+                out[n] = j == 0 ? hs0[i] : fmaf(__builtin_amdgcn_exp2f(sl * A2[n]), hs0[i], loc[n]);
             }
-            st.widen(ld);
         }
-    }
+    };
+    auto sub_start = [&](int j, float (&out)[kN]) {
+        float loc[kN], sl = 0.0f;
+        if (j > 0) ck_load(j, loc, sl);
+        ck_combine(j, loc, sl, out);
+    };
+    sub_start(nsub - 1, h);
 
     // 2. sub-chunks from the last to the first
     float rho[kN], dA[kN];
@@ -307,13 +385,10 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
         }
     };
     issue((nsub - 1) * SUB);
-    float hn[kN];
+    float hn[kN], sn = 0.0f;
     for (int j = nsub - 1; j >= 0; --j) {
         const int t0 = j * SUB;
-        if (j < nsub - 1) {
-#pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = hn[n];
-        }
+        if (j < nsub - 1) ck_combine(j, hn, sn, h);
         // recompute: states before each token, step sizes, dy (and dz)
         float hs[SUB][kN];
         float xs[SUB], dts[SUB], sgs[SUB], dys[SUB];
@@ -361,8 +436,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_bwd(S6BwdArgs a) {
         }
         if (j > 0) {
             issue(t0 - SUB);
-#pragma unroll
-            for (int n = 0; n < kN; ++n) hn[n] = ck[(static_cast<int64_t>(j - 1) * kN + n) * D];
+            if (j > 1) ck_load(j - 1, hn, sn);
         }
         // adjoint back through the sub-chunk
         {
@@ -496,14 +570,11 @@ using namespace s6;
 template <class LD, bool GATED>
 static hipError_t launch_bwd_t(const S6BwdArgs& a, hipStream_t stream) {
     const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
+    dim3 g0(static_cast<unsigned>(nblk * a.n_chunks));
+    s6_timing_mark("s6_chunk_ckpt", stream, true);
+    hipLaunchKernelGGL((s6_chunk_ckpt<LD>), g0, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_chunk_ckpt", stream, false);
     if (a.n_chunks > 1) {
-        S6ScanArgs f{};
-        f.x = a.x; f.delta = a.delta; f.B = a.B; f.C = a.C;
-        f.A = a.A; f.Dskip = a.Dskip; f.dt_bias = a.dt_bias; f.h0 = a.h0;
-        f.carry_S = a.carry_S; f.carry_H = a.carry_H;
-        f.batch = a.batch; f.L = a.L; f.D = a.D; f.chunk_len = a.chunk_len; f.n_chunks = a.n_chunks;
-        f.bf16 = a.bf16; f.pair_loads = a.pair_loads;
-        s6_launch_chunk_carry(f, stream);
         s6_launch_fold(S6FoldArgs{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0},
                        "s6_carry_scan", stream);
         dim3 g1(static_cast<unsigned>(nblk * (a.n_chunks - 1)));

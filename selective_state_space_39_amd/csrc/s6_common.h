@@ -118,7 +118,7 @@ struct S6BwdArgs {
     // workspace
     float* carry_S; float* carry_H;      // forward carries / starting states, (batch, n-1, [N,] D)
     float* rcarry_S; float* rcarry_H;    // adjoint carries / incoming adjoints, same shapes
-    float* ckpt;                         // (batch, n, chunk_len / sub, N, D) sub-chunk starting states
+    float* ckpt;                         // (batch, n, chunk_len / sub, N + 1, D) local sub-chunk states and step sums
     float* part_bc;                      // (batch, L, ceil(D / 64), 2N) per-wavefront dB | dC sums
     float* part_p;                       // (batch, n, N + 2, D) per-chunk dA | dDskip | ddt_bias
     int64_t batch, L, D;

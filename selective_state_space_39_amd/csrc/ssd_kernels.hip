@@ -47,7 +47,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQ = 64;          // tokens per chunk
 constexpr int kP = 64;          // channels per head
 constexpr int kThreads = 256;   // 4 wavefronts
-constexpr int kLdQ = kQ + 8;    // padded LDS row lengths (bf16), against bank conflicts
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint16_t to_bf16(float v) {

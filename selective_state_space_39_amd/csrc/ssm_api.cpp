@@ -198,7 +198,7 @@ int make_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, BwdPla
         return fail(SSM_ERR_SHAPE, "batch * ceil(D / 256) * chunks exceeds the grid limit");
     auto part = [](int64_t floats) { return floats < 0 ? int64_t(-1) : (floats * 4 + 255) / 256 * 256; };
     const int64_t carries = mul_ck(mul_ck(batch, p.n_chunks - 1), D);
-    const int64_t ckpt = mul_ck(mul_ck(mul_ck(mul_ck(batch, p.n_chunks), chunk_len / kBwdSub), kN), D);
+    const int64_t ckpt = mul_ck(mul_ck(mul_ck(mul_ck(batch, p.n_chunks), chunk_len / kBwdSub), kN + 1), D);
     const int64_t bc = mul_ck(mul_ck(mul_ck(batch, L), (D + 63) / 64), 2 * kN);
     const int64_t pp = mul_ck(mul_ck(mul_ck(batch, p.n_chunks), kBwdParams), D);
     const int64_t sizes[7] = {part(carries), part(mul_ck(carries, kN)), part(carries), part(mul_ck(carries, kN)),

@@ -162,14 +162,14 @@ def test_bwd_plan_and_workspace():
     assert binding.bwd_plan(2, 300, 200, 1, 64) == (64, 5)
     carries = 2 * 4 * 200
     expect = (2 * (_part(carries) + _part(carries * 16))     # state and adjoint carries
-              + _part(2 * 5 * (64 // 4) * 16 * 200)          # sub-chunk checkpoints
+              + _part(2 * 5 * (64 // 4) * 17 * 200)          # sub-chunk checkpoints (16 states + step sum)
               + _part(2 * 300 * 4 * 32)                      # per-wavefront dB | dC sums
               + _part(2 * 5 * 18 * 200))                     # per-chunk parameter sums
     assert binding.bwd_workspace_bytes(2, 300, 200, 1, 64) == expect
     # one chunk: no carries, still checkpoints and partial sums
     cl, nc = binding.bwd_plan(1, 40, 16, 0, 64)
     assert (cl, nc) == (64, 1)
-    assert binding.bwd_workspace_bytes(1, 40, 16, 0, 64) == (_part(64 // 4 * 16 * 16) + _part(40 * 1 * 32)
+    assert binding.bwd_workspace_bytes(1, 40, 16, 0, 64) == (_part(64 // 4 * 17 * 16) + _part(40 * 1 * 32)
                                                               + _part(18 * 16))
     for (b, l, d) in [(8, 2048, 1536), (4, 2048, 5120), (1, 131072, 2048), (1, 256, 16)]:
         cl, nc = binding.bwd_plan(b, l, d, 1, 0)
