@@ -133,8 +133,8 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
     except (OSError, ValueError):
         t = {}
     rec = {}
-    for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_chunk_carry_rev",
-                  "s6_chunk_bwd", "s6_reduce_bc", "s6_reduce_params", "ssd_chunked"):
+    for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_bwd_carries",
+                  "s6_carry_scan2", "s6_chunk_bwd", "s6_bwd_reduce", "ssd_chunked"):
         try:
             fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
         except SystemExit:

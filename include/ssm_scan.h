@@ -296,8 +296,8 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
  * ssm_timing_enable(0, NULL) stops recording.  Recording events between
  * kernels costs time, so time whole calls with recording off.  Kernel names:
  * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step", and for the
- * backward "s6_chunk_carry_rev", "s6_carry_scan_rev", "s6_chunk_bwd",
- * "s6_reduce_bc", "s6_reduce_params", and "ssd_chunked".  Returns SSM_OK.
+ * backward "s6_bwd_carries", "s6_carry_scan2", "s6_chunk_bwd",
+ * "s6_bwd_reduce", and "ssd_chunked".  Returns SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the

@@ -17,16 +17,18 @@
 // state: a chunk scanned backward from mu = 0 leaves (S = sum Delta,
 // Lambda = Abar_{t0} mu_{t0}), and the incoming adjoint of chunk c-1 is
 // Lambda_c + exp(A S_c) * (incoming adjoint of chunk c).  Launch order:
-//   1. s6_chunk_ckpt: every chunk scanned from a zero state, storing the local
-//      state at each sub-chunk start and leaving the chunk carry;
-//      s6_carry_scan (the forward's fold): starting state per chunk;
-//   2. s6_chunk_carry_rev: adjoint carries of chunks 1..n-1;
-//      s6_carry_scan in reverse from dh_last: incoming adjoint per chunk;
+//   1. s6_bwd_carries, two independent jobs in one grid so that the
+//      HBM-bound one overlaps the VALU-bound one:
+//      - every chunk scanned from a zero state, storing the local state at
+//        each sub-chunk start and leaving the chunk carry;
+//      - the adjoint carries of chunks 1..n-1;
+//   2. s6_carry_scan2: the forward fold (starting state per chunk) and the
+//      reverse fold from dh_last (incoming adjoint per chunk) in one grid;
 //   3. s6_chunk_bwd: per chunk, sub-chunk by sub-chunk from the end, the
 //      sub-chunk's starting state is rebuilt from its checkpoint, its states are
 //      recomputed into registers and the adjoint runs back through them;
-//   4. s6_reduce_bc / s6_reduce_params: deterministic sums of the per-wavefront
-//      dB, dC and per-chunk dA, dDskip, ddt_bias partials.
+//   4. s6_bwd_reduce: deterministic sums of the per-wavefront dB, dC and the
+//      per-chunk dA, dDskip, ddt_bias partials, one grid for both.
 
 #include "s6_device.h"
 
@@ -70,14 +72,14 @@ __device__ __forceinline__ float gate_grad(float g, float z, float& dz_per_y) {
 // adjoint carries of chunks 1..n-1
 // ---------------------------------------------------------------------------
 template <class LD, bool GATED>
-__global__ __launch_bounds__(kBlock) void s6_chunk_carry_rev(S6BwdArgs a) {
+__device__ __forceinline__ void carry_rev_body(const S6BwdArgs& a, int64_t bid) {
     using IO = typename LD::IO;
     using T = typename IO::T;
     constexpr int NT = GATED ? 3 : 2;          // delta, dout, z
     LD ld;
     constexpr uint32_t es = sizeof(T);
     Geo g;
-    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks - 1, 1, g)) return;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks - 1, 1, g, bid)) return;
     const uint32_t rowb = static_cast<uint32_t>(a.D) * es;
     const uint32_t bytes = static_cast<uint32_t>(g.nt) * rowb;
     const int64_t e0 = g.row0 * a.D;
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry_rev(S6BwdArgs a) {
 // as local + exp(A * sum Delta) * (chunk starting state) instead of re-running
 // the chunk.  Chunks 0..n-2 also leave their carry for the state fold.
 template <class LD>
-__global__ __launch_bounds__(kBlock) void s6_chunk_ckpt(S6BwdArgs a) {
+__device__ __forceinline__ void ckpt_body(const S6BwdArgs& a, int64_t bid) {
     using IO = typename LD::IO;
     using T = typename IO::T;
     constexpr int NT = 2;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_ckpt(S6BwdArgs a) {
     LD ld;
     constexpr uint32_t es = sizeof(T);
     Geo g;
-    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks, 0, g)) return;
+    if (!geo_setup(a.batch, a.L, a.D, a.chunk_len, a.n_chunks, 0, g, bid)) return;
     const uint32_t rowb = static_cast<uint32_t>(a.D) * es;
     const uint32_t last = static_cast<uint32_t>(g.nt - 1) * rowb;
     const int64_t e0 = g.row0 * a.D;
@@ -201,6 +203,17 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_ckpt(S6BwdArgs a) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) a.carry_H[(cs * kN + n) * a.D + g.d] = h[n];
     }
+}
+
+// The checkpoint pass (HBM-bound: it writes the checkpoints) and the adjoint
+// carry pass (VALU-bound) are independent: one launch runs both, so they
+// overlap on the chip.  Workgroups [0, nblk * n) take the first job.
+template <class LD, bool GATED>
+__global__ __launch_bounds__(kBlock) void s6_bwd_carries(S6BwdArgs a) {
+    const int64_t first = (a.D + kBlock - 1) / kBlock * a.batch * a.n_chunks;
+    const int64_t i = blockIdx.x;
+    if (i < first) ckpt_body<LD>(a, i);
+    else carry_rev_body<LD, GATED>(a, i - first);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,8 +527,8 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
 // deterministic reductions of the partial sums
 // ---------------------------------------------------------------------------
 // dB, dC: one lane per (b, t, k), k < 2N; sums the ceil(D / 64) wavefront partials.
-__global__ __launch_bounds__(kBlock) void s6_reduce_bc(S6BwdArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+__device__ __forceinline__ void reduce_bc_body(const S6BwdArgs& a, int64_t bid) {
+    const int64_t i = bid * kBlock + threadIdx.x;
     if (i >= a.batch * a.L * 2 * kN) return;
     const int64_t row = i / (2 * kN);
     const int k = static_cast<int>(i % (2 * kN));
@@ -531,12 +544,12 @@ __global__ __launch_bounds__(kBlock) void s6_reduce_bc(S6BwdArgs a) {
 // wavefronts sum every fourth (batch row, chunk) partial with eight
 // independent accumulators, then wavefront 0 adds the four sums in a fixed
 // order.
-__global__ __launch_bounds__(kBlock) void s6_reduce_params(S6BwdArgs a) {
-    __shared__ float part[kBlock / kWave][kWave];
+__device__ __forceinline__ void reduce_params_body(const S6BwdArgs& a, int64_t bid, float (&part)[kBlock / kWave][kWave]) {
     const int wave = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-    const int64_t k = blockIdx.y;
-    const int64_t dl = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    const int64_t gd = (a.D + kWave - 1) / kWave;
+    const int64_t k = bid / gd;
+    const int64_t dl = (bid % gd) * kWave + lane;
     const int64_t d = dl < a.D ? dl : a.D - 1;
     const int64_t units = a.batch * a.n_chunks;
     const int64_t stride = kBwdParams * a.D;
@@ -560,6 +573,16 @@ __global__ __launch_bounds__(kBlock) void s6_reduce_params(S6BwdArgs a) {
     }
 }
 
+// Both reductions in one launch: workgroups [0, ceil(D / 64) * 18) reduce the
+// parameters, the rest dB and dC.
+__global__ __launch_bounds__(kBlock) void s6_bwd_reduce(S6BwdArgs a) {
+    __shared__ float part[kBlock / kWave][kWave];
+    const int64_t first = (a.D + kWave - 1) / kWave * kBwdParams;
+    const int64_t i = blockIdx.x;
+    if (i < first) reduce_params_body(a, i, part);
+    else reduce_bc_body(a, i - first);
+}
+
 }  // namespace s6
 
 // ---------------------------------------------------------------------------
@@ -570,33 +593,23 @@ using namespace s6;
 template <class LD, bool GATED>
 static hipError_t launch_bwd_t(const S6BwdArgs& a, hipStream_t stream) {
     const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
-    dim3 g0(static_cast<unsigned>(nblk * a.n_chunks));
-    s6_timing_mark("s6_chunk_ckpt", stream, true);
-    hipLaunchKernelGGL((s6_chunk_ckpt<LD>), g0, dim3(kBlock), 0, stream, a);
-    s6_timing_mark("s6_chunk_ckpt", stream, false);
-    if (a.n_chunks > 1) {
-        s6_launch_fold(S6FoldArgs{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0},
-                       "s6_carry_scan", stream);
-        dim3 g1(static_cast<unsigned>(nblk * (a.n_chunks - 1)));
-        s6_timing_mark("s6_chunk_carry_rev", stream, true);
-        hipLaunchKernelGGL((s6_chunk_carry_rev<LD, GATED>), g1, dim3(kBlock), 0, stream, a);
-        s6_timing_mark("s6_chunk_carry_rev", stream, false);
-        s6_launch_fold(S6FoldArgs{a.A, a.dh_last, a.rcarry_S, a.rcarry_H, a.batch, a.D, a.n_chunks - 1, 1},
-                       "s6_carry_scan_rev", stream);
-    }
+    dim3 g0(static_cast<unsigned>(nblk * a.n_chunks + (a.n_chunks > 1 ? nblk * (a.n_chunks - 1) : 0)));
+    s6_timing_mark("s6_bwd_carries", stream, true);
+    hipLaunchKernelGGL((s6_bwd_carries<LD, GATED>), g0, dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_bwd_carries", stream, false);
+    if (a.n_chunks > 1)
+        s6_launch_fold2(S6FoldArgs{a.A, a.h0, a.carry_S, a.carry_H, a.batch, a.D, a.n_chunks - 1, 0},
+                        S6FoldArgs{a.A, a.dh_last, a.rcarry_S, a.rcarry_H, a.batch, a.D, a.n_chunks - 1, 1},
+                        "s6_carry_scan2", stream);
     dim3 g3(static_cast<unsigned>(nblk * a.n_chunks));
     s6_timing_mark("s6_chunk_bwd", stream, true);
     hipLaunchKernelGGL((s6_chunk_bwd<LD, GATED>), g3, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_chunk_bwd", stream, false);
     const int64_t nbc = a.batch * a.L * 2 * kN;
-    s6_timing_mark("s6_reduce_bc", stream, true);
-    hipLaunchKernelGGL(s6_reduce_bc, dim3(static_cast<unsigned>((nbc + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       stream, a);
-    s6_timing_mark("s6_reduce_bc", stream, false);
-    s6_timing_mark("s6_reduce_params", stream, true);
-    hipLaunchKernelGGL(s6_reduce_params, dim3(static_cast<unsigned>((a.D + kWave - 1) / kWave), kBwdParams),
-                       dim3(kBlock), 0, stream, a);
-    s6_timing_mark("s6_reduce_params", stream, false);
+    const int64_t nred = (a.D + kWave - 1) / kWave * kBwdParams + (nbc + kBlock - 1) / kBlock;
+    s6_timing_mark("s6_bwd_reduce", stream, true);
+    hipLaunchKernelGGL(s6_bwd_reduce, dim3(static_cast<unsigned>(nred)), dim3(kBlock), 0, stream, a);
+    s6_timing_mark("s6_bwd_reduce", stream, false);
     return hipGetLastError();
 }
 

@@ -160,6 +160,7 @@ void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin);
 
 hipError_t s6_launch_scan(const S6ScanArgs& a, hipStream_t stream);
 void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream);
+void s6_launch_fold2(const S6FoldArgs& f0, const S6FoldArgs& f1, const char* name, hipStream_t stream);
 void s6_launch_chunk_carry(const S6ScanArgs& a, hipStream_t stream);   // chunks 0 .. n-2
 hipError_t s6_launch_bwd(const S6BwdArgs& a, hipStream_t stream);
 constexpr int kBwdSub = 4;           // tokens per backward sub-chunk (states kept in registers)

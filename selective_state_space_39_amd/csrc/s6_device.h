@@ -133,8 +133,8 @@ constexpr int kXcds = 8;
 // contiguous channel blocks [x * nblk/8, (x+1) * nblk/8) with all their
 // chunks, so a batch row's B/C rows are shared in one L2 and every carry is
 // read on the XCD that wrote it.  Otherwise the plain row-major order is used.
-__device__ __forceinline__ void wg_coords(int64_t nblk, int64_t nchunks, int64_t& blk, int64_t& chunk) {
-    const int64_t i = blockIdx.x;
+__device__ __forceinline__ void wg_coords(int64_t nblk, int64_t nchunks, int64_t& blk, int64_t& chunk,
+                                          int64_t i) {
     if (nblk % kXcds == 0) {
         const int64_t xcd = i % kXcds, pos = i / kXcds;
         blk = xcd * (nblk / kXcds) + pos / nchunks;
@@ -147,11 +147,12 @@ __device__ __forceinline__ void wg_coords(int64_t nblk, int64_t nchunks, int64_t
 
 // Geometry of this lane: chunk index space [chunk_first, chunk_first + nchunks)
 // of a (batch, L, D) problem cut into chunks of chunk_len tokens.
+// bid: the workgroup's index in this job (blockIdx.x unless several jobs share one launch)
 __device__ __forceinline__ bool geo_setup(int64_t batch, int64_t L, int64_t D, int64_t chunk_len,
-                                          int64_t nchunks, int64_t chunk_first, Geo& g) {
+                                          int64_t nchunks, int64_t chunk_first, Geo& g, int64_t bid = -1) {
     const int64_t gx = (D + kBlock - 1) / kBlock;              // channel blocks per batch row
     int64_t blk, chunk;
-    wg_coords(gx * batch, nchunks, blk, chunk);
+    wg_coords(gx * batch, nchunks, blk, chunk, bid < 0 ? static_cast<int64_t>(blockIdx.x) : bid);
     const int64_t bx = blk % gx;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t first = bx * kBlock + wave * kWave;

@@ -167,10 +167,10 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
 // (the same combine: the adjoint obeys the transposed recurrence).
 constexpr int kScanBlk = 16;
 
-__global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) {
+__device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t bid) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t gx = (a.D + kWave - 1) / kWave;               // 64-channel groups per batch row
-    const int64_t unit = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave;
+    const int64_t unit = bid * (kBlock / kWave) + wave;
     if (unit >= a.batch * gx * kN) return;                      // whole wavefront past the end
     const int n = static_cast<int>(unit % kN);
     const int64_t grp = unit / kN;
@@ -202,6 +202,15 @@ __global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) {
             }
         }
     }
+}
+
+__global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) { fold_body(a, blockIdx.x); }
+
+// two independent folds (the backward's state and adjoint carries) in one launch
+__global__ __launch_bounds__(kBlock) void s6_carry_scan2(S6FoldArgs a, S6FoldArgs b, int64_t first) {
+    const int64_t i = blockIdx.x;
+    if (i < first) fold_body(a, i);
+    else fold_body(b, i - first);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,6 +421,14 @@ void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
     dim3 g(static_cast<unsigned>((waves + kBlock / kWave - 1) / (kBlock / kWave)));
     s6_timing_mark(name, stream, true);
     hipLaunchKernelGGL(s6_carry_scan, g, dim3(kBlock), 0, stream, f);
+    s6_timing_mark(name, stream, false);
+}
+
+void s6_launch_fold2(const S6FoldArgs& f0, const S6FoldArgs& f1, const char* name, hipStream_t stream) {
+    const int64_t waves = f0.batch * ((f0.D + kWave - 1) / kWave) * kN;
+    const int64_t per = (waves + kBlock / kWave - 1) / (kBlock / kWave);
+    s6_timing_mark(name, stream, true);
+    hipLaunchKernelGGL(s6_carry_scan2, dim3(static_cast<unsigned>(2 * per)), dim3(kBlock), 0, stream, f0, f1, per);
     s6_timing_mark(name, stream, false);
 }
 
