@@ -63,7 +63,8 @@ KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/s6_kernels.hip",
                   "selective_state_space_39_amd/csrc/s6_device.h",
                   "selective_state_space_39_amd/csrc/s6_common.h"]
 BWD_KERNEL_SOURCES = KERNEL_SOURCES + ["selective_state_space_39_amd/csrc/s6_bwd.hip"]
-SSD_KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/ssd_kernels.hip", "selective_state_space_39_amd/csrc/s6_common.h"]
+SSD_KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/ssd_kernels.hip", "selective_state_space_39_amd/csrc/ssd_common.h",
+                      "selective_state_space_39_amd/csrc/s6_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

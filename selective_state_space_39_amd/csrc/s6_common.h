@@ -137,23 +137,6 @@ struct S6FoldArgs {
     int reverse;         // fold carries ncar-1 .. 0 instead of 0 .. ncar-1
 };
 
-// SSD (Mamba-2 style) layer: scalar decay per head, P = 64 channels per head.
-struct SsdArgs {
-    const void* x;       // (batch, L, H, 64) bf16
-    const void* delta;   // (batch, L, H) bf16
-    const void* z;       // (batch, L, H, 64) bf16 or NULL
-    const void* B;       // (batch, L, N) bf16
-    const void* C;       // (batch, L, N) bf16
-    const float* A;      // (H)
-    const float* Dskip;  // (H)
-    const float* dt_bias;// (H)
-    const float* h0;     // (batch, H, 64, N) or NULL
-    void* y;             // (batch, L, H, 64) bf16
-    float* h_last;       // (batch, H, 64, N) or NULL
-    int64_t batch, L, H, N;
-};
-hipError_t ssd_launch(const SsdArgs& a, hipStream_t stream);
-
 // Optional per-launch timing (ssm_timing_enable): called before and after
 // every kernel launch with the launch's stream.
 void s6_timing_mark(const char* kernel, hipStream_t stream, bool begin);

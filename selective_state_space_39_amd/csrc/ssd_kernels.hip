@@ -36,7 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "s6_common.h"
+#include "ssd_common.h"
 
 namespace ssd {
 

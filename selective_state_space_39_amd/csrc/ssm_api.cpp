@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "s6_common.h"
+#include "ssd_common.h"
 
 namespace {
 
