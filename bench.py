@@ -150,7 +150,7 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
     print(json.dumps(t[workload]))
 
 
-def cpu_baseline(s, min_seconds=10.0, max_passes=3):
+def cpu_baseline(s, min_seconds=10.0, max_passes=12):
     """The float64 oracle as it stands, on the host, over whole passes of the workload."""
     import numpy as np
     import oracle
