@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum {
     SSM_F32 = 0,   /* float32 */
@@ -276,8 +276,15 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  *   B, C      (batch, L, N) bf16, N = 64 or 128, 16-byte aligned.
  *   A, Dskip, dt_bias (H) float32.
  *   h0, h_last (batch, H, 64, N) float32, 16-byte aligned; NULL = zeros / not wanted.
+ *   workspace at least ssm_ssd_fwd_workspace_bytes(...) bytes of device
+ *             memory, 16-byte aligned, owned by the caller, contents ignored;
+ *             it receives C_t . B_i of every chunk (fp32, no head in it), which
+ *             all heads of a batch row share.  It must not overlap any argument
+ *             and must not be used by another call until this one's work on
+ *             the stream is done.
  * io_dtype must be SSM_BF16 (SSM_ERR_DTYPE otherwise); N other than 64 or
- * 128 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE.  No workspace.
+ * 128 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE; a missing or small
+ * workspace is SSM_ERR_WORKSPACE.
  */
 int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
                 const void* B, const void* C,
@@ -285,7 +292,11 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
                 const float* h0,
                 void* y, float* h_last,
                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
-                void* stream);
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes ssm_ssd_fwd needs: batch * ceil(L / 64) * 16384.  Negative
+ * ssm_status for an invalid shape.  Host-only; touches no device. */
+int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype);
 
 /*
  * Per-kernel timing, for measurement tools; not needed to compute anything.
@@ -297,7 +308,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
  * kernels costs time, so time whole calls with recording off.  Kernel names:
  * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step", and for the
  * backward "s6_bwd_carries", "s6_carry_scan2", "s6_chunk_bwd",
- * "s6_bwd_reduce", and "ssd_chunked".  Returns SSM_OK.
+ * "s6_bwd_reduce", and for the SSD layer "ssd_gram", "ssd_chunked".  Returns SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the

@@ -15,7 +15,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssm_scan.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 N_STATE = 16
 SSM_F32, SSM_BF16 = 0, 1
 
@@ -52,7 +52,9 @@ def lib() -> ctypes.CDLL:
     L.ssm_conv_state_update.restype = i32
     L.ssm_conv_state_update.argtypes = [vp] * 5 + [i64] + [vp] * 8 + [i64, i64, i64, i32, vp]
     L.ssm_ssd_fwd.restype = i32
-    L.ssm_ssd_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i64, i32, vp]
+    L.ssm_ssd_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i64, i32, vp, i64, vp]
+    L.ssm_ssd_fwd_workspace_bytes.restype = i64
+    L.ssm_ssd_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     L.ssm_scan_bwd_plan.restype = i32
@@ -346,12 +348,23 @@ def conv_state_update(h, conv_state, xin, conv_w, conv_b, delta, A, B, C, D, dt_
     return y
 
 
-def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: bool = True, out=None):
+def ssd_workspace_bytes(batch: int, L: int, H: int, N: int, P: int = 64) -> int:
+    """Device bytes ssd_fwd needs as workspace (the per-chunk C . B products)."""
+    n = lib().ssm_ssd_fwd_workspace_bytes(batch, L, H, P, N, SSM_BF16)
+    if n < 0:
+        _check(n)
+    return n
+
+
+def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: bool = True, out=None,
+            workspace=None):
     """SSD (Mamba-2 style) layer with a scalar decay per head.
 
     x, z: (batch, L, H, 64); delta: (batch, L, H); B, C: (batch, L, N) with N
     = 64 or 128, all bfloat16; A, D, dt_bias: (H,) float32; h0: (batch, H,
-    64, N) float32.  Returns (y, h_last).
+    64, N) float32; workspace: a device tensor of at least
+    ssd_workspace_bytes(...) bytes (allocated here when None).  Returns
+    (y, h_last).
     """
     if x.dim() != 4:
         raise ValueError("x must be (batch, L, H, P)")
@@ -373,8 +386,16 @@ def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: b
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", (batch, L, H, P), dt, dev)
     h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev) if return_last_state else None
+    if io == SSM_BF16 and N in (64, 128) and P == 64:
+        nws = ssd_workspace_bytes(batch, L, H, N, P)
+        if workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        elif workspace.numel() * workspace.element_size() < nws:
+            raise ValueError(f"workspace too small: {nws} bytes needed")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
-                           _ptr(h0), _ptr(y), _ptr(h_last), batch, L, H, P, N, io, _stream(dev))
+                           _ptr(h0), _ptr(y), _ptr(h_last), batch, L, H, P, N, io, _ptr(workspace), nbytes,
+                           _stream(dev))
     _check(rc)
     return y, h_last
 

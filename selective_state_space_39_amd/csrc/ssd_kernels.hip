@@ -1,37 +1,37 @@
-// gfx950 kernel of the SSD (Mamba-2 style) layer: scalar decay per head, so
+// gfx950 kernels of the SSD (Mamba-2 style) layer: scalar decay per head, so
 // the causal matrix mixer of "Mamba", "Relation to Mamba-2" becomes, inside a
 // chunk, a masked dense product, and across chunks a carried P x N state per
 // head ("Mamba & State-Space Sequence Models", "Core mechanics": the duality
 // of structured SSMs and a class of linear attention).
 //
-// One workgroup (4 wavefronts) per (batch row, head) walks its chunks of
-// kQ = 64 tokens in order.  With S_t = A_h * (sum of Delta up to t inside the
+// Chunks of kQ = 64 tokens.  With S_t = A_h * (sum of Delta up to t inside the
 // chunk):
-//   G^T[i][t]  = B_i . C_t                                   (MFMA over N)
-//   M[t][i]    = G^T[i][t] exp(S_t - S_i) Delta_i,  i <= t    (mask, VALU)
-//   y_t        = sum_i M[t][i] x_i                            (MFMA over i)
-//              + exp(S_t) C_t . state_in                      (MFMA over N)
-//              + D_h x_t, then * silu(z_t)
-//   state_out  = exp(S_end) state_in + sum_i exp(S_end - S_i) Delta_i x_i B_i^T   (MFMA over i)
-// The state (P x N fp32) lives in MFMA accumulators for the whole sequence;
-// its bf16 copy in LDS feeds the next chunk's state term.  Operands are bf16
-// (the io dtype), accumulation fp32.
+//   G[t][i]    = C_t . B_i                       (no head in it: ssd_gram, once
+//                                                 per batch row and chunk)
+//   M[t][i]    = G[t][i] exp(S_t - S_i) Delta_i, i <= t
+//   y_t        = sum_i M[t][i] x_i + exp(S_t) state_in C_t + D_h x_t, then * silu(z_t)
+//   state_out  = exp(S_end) state_in + sum_i exp(S_end - S_i) Delta_i x_i B_i^T
+// ssd_chunked: one workgroup (4 wavefronts) per (batch row, head) walks its
+// chunks in order.  Wavefront w computes the outputs of tokens 16w .. 16w+15
+// (its C rows come straight from memory into MFMA operand registers, its M
+// entries from G in registers) and owns channels 16w .. 16w+15 of the fp32
+// state, kept in MFMA accumulators for the whole sequence; a bf16 copy of the
+// state in LDS feeds every wavefront's state term.  Operands are bf16 (the io
+// dtype), accumulation fp32.
 //
 // v_mfma_f32_16x16x32_bf16 operand layout (lane l, r = l % 16, q = l / 16):
 // A: A[m = r][k = 8q .. 8q+7]; B: B[k = 8q .. 8q+7][n = r]; D: D[m = 4q + i][n = r].
-// Because a contraction does not care about the order of k, the mask's
-// accumulator tiles (G^T rows i = 4q .. 4q+3 of two 16-row tiles) are used
-// directly as the A operand of the y product, with the x operand read in the
-// same permuted k order.
+// Outputs are computed transposed (m = channel, n = token), so a lane ends
+// with 4 consecutive channels of one token: 8-byte gate loads and stores.
 //
 // Operands whose contraction index runs along the rows of a row-major LDS
-// tile (B and the weighted x in the state update, x in the intra-chunk
-// product) are fetched with gfx950's transposing LDS read ds_read_b64_tr_b16:
-// within each 16-lane group, output lane j = 4a + c, element s comes from
-// the 8-byte segment addressed by lane 4s + a, element c.  Addressing lane
-// 4s + a at row (row0 + s), columns col0 + 4a .. 4a+3 therefore hands lane j
-// the column col0 + j of rows row0 .. row0+3 -- the k-major operand layout --
-// so no tile is ever stored transposed.
+// tile (x in both products, B in the state update) are fetched with gfx950's
+// transposing LDS read ds_read_b64_tr_b16: within each 16-lane group, output
+// lane j = 4a + c, element s comes from the 8-byte segment addressed by lane
+// 4s + a, element c.  Addressing lane 4s + a at row (row0 + s), columns
+// col0 + 4a .. 4a+3 therefore hands lane j the column col0 + j of rows
+// row0 .. row0+3 -- the k-major operand layout -- so no tile is ever stored
+// transposed.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -74,19 +74,19 @@ __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
                                                  pack2(v[6], v[7])));
 }
 
+// LDS of ssd_chunked: 48 KB for N = 128, so three workgroups fit on a CU
+// and every (batch row, head) of a 640-sequence launch is resident at once.
 template <int N>
 struct alignas(16) Smem {
-    static constexpr int kLdB = N + 24;   // 16-byte reads and transposing reads both conflict-free
-    static constexpr int kLdC = N + 24;
+    static constexpr int kLdB = N + 24;   // transposing reads conflict-free
+    static constexpr int kLdS = N + 8;    // 16-byte reads and 8-byte writes conflict-free
     static constexpr int kLdX = kP + 16;
-    static constexpr int kLdM = kQ + 8;
-    uint16_t Bs[kQ][kLdB];      // B rows of the chunk          [i][n]
-    uint16_t Cs[kQ][kLdC];      // C rows of the chunk          [t][n]
-    uint16_t Xs[kQ][kLdX];      // x rows                       [i][p]
-    uint16_t XWs[kQ][kLdX];     // exp(S_end - S_i) Delta_i x_i [i][p]
-    uint16_t Ms[kQ][kLdM];      // masked mixer M[t][i] = (B_i . C_t) exp(S_t - S_i) Delta_i, i <= t
+    uint16_t Bs[kQ][kLdB];      // B rows of the chunk            [i][n]
+    uint16_t Xs[kQ][kLdX];      // x rows                         [i][p]
+    uint16_t St[kP][kLdS];      // bf16 copy of the incoming state [p][n]
     float S2[kQ];               // S_t * log2(e)
     float Dl[kQ];               // Delta_t
+    float Wt[kQ];               // exp(S_end - S_t) Delta_t
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -104,12 +104,6 @@ __device__ __forceinline__ bf16x8 opnd_rows8(const uint16_t* base, int ld, int r
     const v4s lo = tr4(p), hi = tr4(p + 4 * ld);
     return __builtin_bit_cast(bf16x8, static_cast<v8s>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
 }
-// two 8-byte halves of one row: elements col0 .. col0+3 and col1 .. col1+3
-__device__ __forceinline__ bf16x8 lds4x2(const uint16_t* row, int col0, int col1) {
-    const uint2 a = *reinterpret_cast<const uint2*>(row + col0);
-    const uint2 b = *reinterpret_cast<const uint2*>(row + col1);
-    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
 
 // Every tensor of one (batch row, head) sequence is addressed through a buffer
 // resource based at its first element and bounded by its last row: a lane's
@@ -120,98 +114,156 @@ constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format (g
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
+// ---------------------------------------------------------------------------
+// ssd_gram: G[t][i] = C_t . B_i (fp32) for every (batch row, chunk), the part
+// of the mixer that no head changes.  Workgroup = (batch row, chunk);
+// wavefront w computes rows t = 16w .. 16w+15.  Rows past the sequence end
+// read B, C as zero, so their G is zero.
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_gram(SsdArgs a) {
+    constexpr int KS = N / 32;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+    const int64_t nch = (a.L + kQ - 1) / kQ;
+    const int64_t b = blockIdx.x / nch, c = blockIdx.x % nch;
+    const __amdgpu_buffer_rsrc_t rB = rsrc(static_cast<const uint16_t*>(a.B) + b * a.L * N, a.L * N * 2);
+    const __amdgpu_buffer_rsrc_t rC = rsrc(static_cast<const uint16_t*>(a.C) + b * a.L * N, a.L * N * 2);
+    const uint32_t so = static_cast<uint32_t>(c * kQ * N * 2);
+    // B operand: C rows t = 16w + r, n = 32ks + 8q .. +7
+    bf16x8 cop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        cop[ks] = __builtin_bit_cast(bf16x8, ld16(rC, ((16 * w + r) * N + 32 * ks + 8 * q) * 2, so));
+    float* g = a.gram + ((b * nch + c) * kQ + 16 * w + r) * kQ;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+        // A operand: B rows i = 16ib + r; D[m = i][n = t]: lane slot j = G[t = 16w + r][i = 16ib + 4q + j]
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            acc = mfma(__builtin_bit_cast(bf16x8, ld16(rB, ((16 * ib + r) * N + 32 * ks + 8 * q) * 2, so)), cop[ks], acc);
+        *reinterpret_cast<float4*>(g + 16 * ib + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ssd_chunked
+// ---------------------------------------------------------------------------
 struct SeqIO {
-    __amdgpu_buffer_rsrc_t x, z, y, B, C, dl;
+    __amdgpu_buffer_rsrc_t x, z, y, B, C, dl, G;
     uint32_t xrow, bcrow, dlrow;             // bytes per token row
+    uint32_t gchunk;                         // bytes of G per chunk
 };
 
-// Global data of one chunk, held in registers until it is staged (prefetch).
+// x and B of one chunk in registers until they are staged in LDS (prefetch).
 template <int N>
-struct ChunkRegs {
+struct StageRegs {
     static constexpr int kXSeg = kQ * kP / 8 / kThreads;    // 16-byte pieces of x per thread
-    static constexpr int kBSeg = kQ * N / 8 / kThreads;     // of B (and of C)
-    uint4 x[kXSeg], b[kBSeg], c[kBSeg];
-    uint16_t dl;               // delta of token (lane)
+    static constexpr int kBSeg = kQ * N / 8 / kThreads;     // of B
+    uint4 x[kXSeg], b[kBSeg];
+    uint16_t dl;               // delta of token (lane), wavefront 0 only
 };
 
 template <int N>
-__device__ __forceinline__ void load_chunk(const SeqIO& io, int t0, ChunkRegs<N>& r) {
-    const int tid = threadIdx.x, l = tid & 63;
+__device__ __forceinline__ void load_stage(const SeqIO& io, int t0, int w, StageRegs<N>& r) {
+    const int tid = threadIdx.x;
     const uint32_t so = static_cast<uint32_t>(t0);
 #pragma unroll
-    for (int k = 0; k < ChunkRegs<N>::kXSeg; ++k) {
+    for (int k = 0; k < StageRegs<N>::kXSeg; ++k) {
         const int s = tid + kThreads * k, t = s / (kP / 8), p0 = (s % (kP / 8)) * 8;
-        r.x[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              io.x, t * io.xrow + p0 * 2, so * io.xrow, 0));
+        r.x[k] = ld16(io.x, t * io.xrow + p0 * 2, so * io.xrow);
     }
 #pragma unroll
-    for (int k = 0; k < ChunkRegs<N>::kBSeg; ++k) {
+    for (int k = 0; k < StageRegs<N>::kBSeg; ++k) {
         const int s = tid + kThreads * k, t = s / (N / 8), n0 = (s % (N / 8)) * 8;
-        r.b[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(io.B, t * io.bcrow + n0 * 2,
-                                                                                so * io.bcrow, 0));
-        r.c[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(io.C, t * io.bcrow + n0 * 2,
-                                                                                so * io.bcrow, 0));
+        r.b[k] = ld16(io.B, t * io.bcrow + n0 * 2, so * io.bcrow);
     }
-    r.dl = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(io.dl, l * io.dlrow, so * io.dlrow, 0));
+    if (w == 0)
+        r.dl = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(io.dl, (tid & 63) * io.dlrow,
+                                                                          so * io.dlrow, 0));
 }
 
-// The gate at this lane's outputs: t = 16 tb + r, p = 16 w + 4 q .. +3 (8 bytes per t-block).
-__device__ __forceinline__ void load_gate(const SeqIO& io, int t0, int w, uint2 (&z)[4]) {
-    const int l = threadIdx.x & 63, rr = l & 15, q = l >> 4;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-        z[tb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                              io.z, (16 * tb + rr) * io.xrow + (16 * w + 4 * q) * 2,
-                                              static_cast<uint32_t>(t0) * io.xrow, 0));
-}
-
-// Stage one chunk into LDS.  Every wavefront scans the step sizes itself (lane
-// = token), so the weighted x needs no barrier: a lane takes S_t and Delta_t
-// of its rows from the scanning lanes.
+// What wavefront w reads from memory for its own tokens t = 16w + r: C rows
+// (the B operand of the state term), G rows (for M), the gate.
 template <int N>
-__device__ __forceinline__ void stage_chunk(Smem<N>& sm, const ChunkRegs<N>& r, int nt, float A, float bias, int w) {
-    const int tid = threadIdx.x, l = tid & 63;
-    const float dt = l < nt ? s6::softplus(from_bf16(r.dl) + bias) : 0.0f;
-    float s = dt * A * kLog2e;
+struct OwnRegs {
+    static constexpr int KS = N / 32;
+    bf16x8 c[KS];              // C[t][32ks + 8q .. +7]
+    float4 g[2][2];            // G[t][32ks + 8q .. +7], ks < 1 + (w >= 2)
+    uint2 z[4];                // z[t][16pb + 4q .. +3]
+};
+
+template <int N, bool GATED>
+__device__ __forceinline__ void load_own(const SeqIO& io, int c, int t0, int w, OwnRegs<N>& o) {
+    const int l = threadIdx.x & 63, r = l & 15, q = l >> 4, t = 16 * w + r;
+    const uint32_t so = static_cast<uint32_t>(t0);
 #pragma unroll
-    for (int off = 1; off < kQ; off <<= 1) {                   // inclusive scan over the wavefront
-        const float o = __shfl_up(s, off);
-        if (l >= off) s += o;
+    for (int ks = 0; ks < OwnRegs<N>::KS; ++ks)
+        o.c[ks] = __builtin_bit_cast(bf16x8, ld16(io.C, t * io.bcrow + (32 * ks + 8 * q) * 2, so * io.bcrow));
+    const uint32_t gs = static_cast<uint32_t>(c) * io.gchunk;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks == 0 || w >= 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o.g[ks][h] = __builtin_bit_cast(float4, ld16(io.G, (t * kQ + 32 * ks + 8 * q + 4 * h) * 4, gs));
+        }
     }
+    if constexpr (GATED) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+            o.z[pb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   io.z, t * io.xrow + (16 * pb + 4 * q) * 2, so * io.xrow, 0));
+    }
+}
+
+// Stage one chunk: x and B rows into LDS; wavefront 0 scans the step sizes
+// (lane = token) and publishes S, Delta and the state-update weights.
+template <int N>
+__device__ __forceinline__ void stage_chunk(Smem<N>& sm, const StageRegs<N>& r, int nt, float A, float bias, int w) {
+    const int tid = threadIdx.x, l = tid & 63;
     if (w == 0) {
+        const float dt = l < nt ? s6::softplus(from_bf16(r.dl) + bias) : 0.0f;
+        float s = dt * A * kLog2e;
+#pragma unroll
+        for (int off = 1; off < kQ; off <<= 1) {               // inclusive scan over the wavefront
+            const float o = __shfl_up(s, off);
+            if (l >= off) s += o;
+        }
+        const float s_end = __shfl(s, kQ - 1);
         sm.S2[l] = s;
         sm.Dl[l] = dt;
+        sm.Wt[l] = __builtin_amdgcn_exp2f(s_end - s) * dt;
     }
-    const float s_end = __shfl(s, kQ - 1);
 #pragma unroll
-    for (int k = 0; k < ChunkRegs<N>::kBSeg; ++k) {
+    for (int k = 0; k < StageRegs<N>::kBSeg; ++k) {
         const int e = tid + kThreads * k, t = e / (N / 8), n0 = (e % (N / 8)) * 8;
         *reinterpret_cast<uint4*>(&sm.Bs[t][n0]) = r.b[k];
-        *reinterpret_cast<uint4*>(&sm.Cs[t][n0]) = r.c[k];
     }
 #pragma unroll
-    for (int k = 0; k < ChunkRegs<N>::kXSeg; ++k) {
+    for (int k = 0; k < StageRegs<N>::kXSeg; ++k) {
         const int e = tid + kThreads * k, t = e / (kP / 8), p0 = (e % (kP / 8)) * 8;
         *reinterpret_cast<uint4*>(&sm.Xs[t][p0]) = r.x[k];
-        const float wt = __builtin_amdgcn_exp2f(s_end - __shfl(s, t)) * __shfl(dt, t);
-        const uint32_t w4[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = pack2(wt * lo_bf16(w4[j]), wt * hi_bf16(w4[j]));
-        *reinterpret_cast<uint4*>(&sm.XWs[t][p0]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
-// The ten 16 x 16 tiles (i-block, t-block) of the causal mixer, dealt to the
-// four wavefronts round-robin.
-__device__ __forceinline__ void tile_of(int k, int& ib, int& tb) {
-    tb = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
-    ib = k - tb * (tb + 1) / 2;
+// bf16 copy of this wavefront's state channels into St[p][n]
+template <int N>
+__device__ __forceinline__ void publish_state(Smem<N>& sm, const f32x4 (&st)[N / 16], int w) {
+    const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb)
+        *reinterpret_cast<uint2*>(&sm.St[16 * w + r][16 * nb + 4 * q]) =
+            make_uint2(pack2(st[nb][0], st[nb][1]), pack2(st[nb][2], st[nb][3]));
 }
 
 template <int N, bool GATED>
-__global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
     constexpr int NB = N / 16;            // 16-row blocks of the state's n
     constexpr int KS = N / 32;            // k-steps of a product over n
     __shared__ Smem<N> sm;
@@ -219,7 +271,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, r = l & 15, q = l >> 4;
-    // (batch row, head): the heads of one batch row stay on one XCD (shared B / C rows in its L2)
+    const int tw = 16 * w + r;            // this lane's token inside a chunk
+    const int nks = w >= 2 ? 2 : 1;       // k-steps of 32 tokens that reach token 16w + 15
+    // (batch row, head): the heads of one batch row stay on one XCD (shared B, C, G rows in its L2)
     const int64_t units = a.batch * a.H;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (u % 8) * (units / 8) + u / 8;
@@ -227,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
     const float A = a.A[h], bias = a.dt_bias[h], Dd = a.Dskip[h];
 
     // This wavefront owns channels p = 16 w .. 16 w + 15 of the state: tiles
-    // state^T[n-block nb][p-block w], lane slot i = state^T[16 nb + 4q + i][16 w + r].
+    // state^T[n-block nb][p-block w], lane slot j = state^T[16 nb + 4q + j][16 w + r].
     f32x4 st[NB];
     const float* h0 = a.h0 ? a.h0 + (b * a.H + h) * kP * N : nullptr;
 #pragma unroll
@@ -239,9 +293,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
             st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // the upper-triangle tiles of M that the y product reads are never written: zero them once
-    for (int e = tid; e < kQ * Smem<N>::kLdM; e += kThreads) (&sm.Ms[0][0])[e] = 0;
+    publish_state<N>(sm, st, w);
 
+    const int nchunks = static_cast<int>((a.L + kQ - 1) / kQ);
     SeqIO io;
     {
         const int64_t xoff = (b * a.L * a.H + h) * kP;                       // first element of the sequence
@@ -249,104 +303,103 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
         io.xrow = static_cast<uint32_t>(a.H * kP * 2);
         io.bcrow = N * 2;
         io.dlrow = static_cast<uint32_t>(a.H * 2);
+        io.gchunk = kQ * kQ * 4;
         io.x = rsrc(static_cast<const uint16_t*>(a.x) + xoff, xbytes);
         io.z = rsrc(a.z ? static_cast<const uint16_t*>(a.z) + xoff : nullptr, a.z ? xbytes : 0);
         io.y = rsrc(static_cast<uint16_t*>(a.y) + xoff, xbytes);
         io.B = rsrc(static_cast<const uint16_t*>(a.B) + b * a.L * N, a.L * N * 2);
         io.C = rsrc(static_cast<const uint16_t*>(a.C) + b * a.L * N, a.L * N * 2);
         io.dl = rsrc(static_cast<const uint16_t*>(a.delta) + b * a.L * a.H + h, ((a.L - 1) * a.H + 1) * 2);
+        io.G = rsrc(a.gram + b * nchunks * kQ * kQ, static_cast<int64_t>(nchunks) * kQ * kQ * 4);
     }
-    const int nchunks = static_cast<int>((a.L + kQ - 1) / kQ);
-    ChunkRegs<N> cr;
-    load_chunk<N>(io, 0, cr);
-    uint2 zc[4];
-    if constexpr (GATED) load_gate(io, 0, w, zc);
+    StageRegs<N> sr;
+    OwnRegs<N> own;
+    load_stage<N>(io, 0, w, sr);
+    load_own<N, GATED>(io, 0, 0, w, own);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * kQ;
         const int nt = static_cast<int>(a.L - t0 < kQ ? a.L - t0 : kQ);
-        __syncthreads();                               // previous chunk's LDS reads are done
-        stage_chunk<N>(sm, cr, nt, A, bias, w);
-        __syncthreads();
+        stage_chunk<N>(sm, sr, nt, A, bias, w);
+        __syncthreads();                               // chunk staged, incoming state published
         const int t1 = t0 + kQ;
-        if (c + 1 < nchunks) load_chunk<N>(io, t1, cr);
+        if (c + 1 < nchunks) load_stage<N>(io, t1, w, sr);
 
-        // --- this wavefront's tiles of the masked mixer, into LDS
+        // M^T as the B operand of y^T: lane (r, q) holds M[t = 16w + r][i = 32ks + 8q .. +7]
+        const float s2t = sm.S2[tw];
+        bf16x8 mop[2];
 #pragma unroll
-        for (int slot = 0; slot < 3; ++slot) {
-            const int k = w + 4 * slot;
-            if (k < 10) {
-                int ib, tb;
-                tile_of(k, ib, tb);
-                f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks < nks) {
+                const int i0 = 32 * ks + 8 * q;
+                const float4 sa = *reinterpret_cast<const float4*>(&sm.S2[i0]);
+                const float4 sb = *reinterpret_cast<const float4*>(&sm.S2[i0 + 4]);
+                const float4 da = *reinterpret_cast<const float4*>(&sm.Dl[i0]);
+                const float4 db = *reinterpret_cast<const float4*>(&sm.Dl[i0 + 4]);
+                const float si[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+                const float di[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+                const float gi[8] = {own.g[ks][0].x, own.g[ks][0].y, own.g[ks][0].z, own.g[ks][0].w,
+                                     own.g[ks][1].x, own.g[ks][1].y, own.g[ks][1].z, own.g[ks][1].w};
+                float m[8];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    g = mfma(lds8(&sm.Bs[ib * 16 + r][ks * 32 + 8 * q]), lds8(&sm.Cs[tb * 16 + r][ks * 32 + 8 * q]), g);
-                const int t = tb * 16 + r;
-                const float st2 = sm.S2[t];
-                float m4[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = ib * 16 + 4 * q + j;
-                    const float m = __builtin_amdgcn_exp2f(st2 - sm.S2[i]) * sm.Dl[i];
-                    m4[j] = i <= t ? g[j] * m : 0.0f;
-                }
-                *reinterpret_cast<uint2*>(&sm.Ms[t][ib * 16 + 4 * q]) = make_uint2(pack2(m4[0], m4[1]),
-                                                                                    pack2(m4[2], m4[3]));
+                for (int j = 0; j < 8; ++j)
+                    m[j] = i0 + j <= tw ? gi[j] * (__builtin_amdgcn_exp2f(s2t - si[j]) * di[j]) : 0.0f;
+                mop[ks] = pack8(m);
             }
         }
-        // the incoming state as the bf16 A operand of the state term (m = p, k = n in the permuted order)
-        bf16x8 sa[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const float v8[8] = {st[2 * ks][0], st[2 * ks][1], st[2 * ks][2], st[2 * ks][3],
-                                 st[2 * ks + 1][0], st[2 * ks + 1][1], st[2 * ks + 1][2], st[2 * ks + 1][3]};
-            sa[ks] = pack8(v8);
-        }
-        __syncthreads();                               // M complete
+        const float e = __builtin_amdgcn_exp2f(s2t);
 
-        // --- y^T for this wavefront's 16 channels and every t-block:
-        //     lane slot j = y[t = 16 tb + r][p = 16 w + 4 q + j]
+        // y^T for this wavefront's tokens and every channel block:
+        //     lane slot j = y[t = 16w + r][p = 16pb + 4q + j]
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 yd = f32x4{0.f, 0.f, 0.f, 0.f}, yo = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int pb = 0; pb < 4; ++pb) {
+            f32x4 yi = f32x4{0.f, 0.f, 0.f, 0.f}, ys = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb <= tb / 2; ++kb)
-                yd = mfma(opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, kb * 32 + 8 * q, w * 16),
-                          lds8(&sm.Ms[tb * 16 + r][kb * 32 + 8 * q]), yd);
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < nks) yi = mfma(opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, 32 * ks + 8 * q, 16 * pb), mop[ks], yi);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                yo = mfma(sa[ks], lds4x2(&sm.Cs[tb * 16 + r][0], ks * 32 + 4 * q, ks * 32 + 16 + 4 * q), yo);
-            // rows past the sequence end: stored through the bounded buffer, i.e. dropped
-            const int t = tb * 16 + r;
-            const float e = __builtin_amdgcn_exp2f(sm.S2[t]);
-            const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xs[t][w * 16 + 4 * q]);
-            float yv[4] = {yd[0] + e * yo[0] + Dd * lo_bf16(xv.x), yd[1] + e * yo[1] + Dd * hi_bf16(xv.x),
-                           yd[2] + e * yo[2] + Dd * lo_bf16(xv.y), yd[3] + e * yo[3] + Dd * hi_bf16(xv.y)};
+                ys = mfma(lds8(&sm.St[16 * pb + r][32 * ks + 8 * q]), own.c[ks], ys);
+            const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xs[tw][16 * pb + 4 * q]);
+            float yv[4] = {yi[0] + e * ys[0] + Dd * lo_bf16(xv.x), yi[1] + e * ys[1] + Dd * hi_bf16(xv.x),
+                           yi[2] + e * ys[2] + Dd * lo_bf16(xv.y), yi[3] + e * ys[3] + Dd * hi_bf16(xv.y)};
             if constexpr (GATED) {
-                yv[0] *= s6::silu(lo_bf16(zc[tb].x));
-                yv[1] *= s6::silu(hi_bf16(zc[tb].x));
-                yv[2] *= s6::silu(lo_bf16(zc[tb].y));
-                yv[3] *= s6::silu(hi_bf16(zc[tb].y));
+                yv[0] *= s6::silu(lo_bf16(own.z[pb].x));
+                yv[1] *= s6::silu(hi_bf16(own.z[pb].x));
+                yv[2] *= s6::silu(lo_bf16(own.z[pb].y));
+                yv[3] *= s6::silu(hi_bf16(own.z[pb].y));
             }
+            // rows past the sequence end: stored through the bounded buffer, i.e. dropped
             const uint2 o = make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, o), io.y, t * io.xrow + (w * 16 + 4 * q) * 2,
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, o), io.y, tw * io.xrow + (16 * pb + 4 * q) * 2,
                                                   static_cast<uint32_t>(t0) * io.xrow, 0);
         }
-        if constexpr (GATED) {
-            if (c + 1 < nchunks) load_gate(io, t1, w, zc);
-        }
-        // --- state update: state^T = exp(S_end) state^T + B^T (w x)
+        if (c + 1 < nchunks) load_own<N, GATED>(io, c + 1, t1, w, own);
+
+        // --- state update: state^T = exp(S_end) state^T + B^T (W x), W_i = exp(S_end - S_i) Delta_i
         const float dec = __builtin_amdgcn_exp2f(sm.S2[kQ - 1]);
-        const bf16x8 xw0 = opnd_rows8(&sm.XWs[0][0], Smem<N>::kLdX, 8 * q, w * 16);
-        const bf16x8 xw1 = opnd_rows8(&sm.XWs[0][0], Smem<N>::kLdX, 32 + 8 * q, w * 16);
+        bf16x8 xw[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int i0 = 32 * ks + 8 * q;
+            const bf16x8 xv = opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, i0, 16 * w);
+            const float4 wa = *reinterpret_cast<const float4*>(&sm.Wt[i0]);
+            const float4 wb = *reinterpret_cast<const float4*>(&sm.Wt[i0 + 4]);
+            const float wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(xv[j]) * wi[j];
+            xw[ks] = pack8(v);
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             f32x4 sv = st[nb] * dec;
-            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw0, sv);
-            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw1, sv);
+            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw[0], sv);
+            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw[1], sv);
             st[nb] = sv;
         }
+        __syncthreads();                               // every read of St, Xs, Bs of this chunk is done
+        publish_state<N>(sm, st, w);
     }
     if (a.h_last) {
         float* hl = a.h_last + (b * a.H + h) * kP * N;
@@ -361,8 +414,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunked(SsdArgs a) {
 
 using namespace ssd;
 
+int64_t ssd_gram_bytes(int64_t batch, int64_t L) { return batch * ((L + kQ - 1) / kQ) * kQ * kQ * 4; }
+
 template <int N>
 static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
+    dim3 g0(static_cast<unsigned>(a.batch * ((a.L + kQ - 1) / kQ)));
+    s6_timing_mark("ssd_gram", stream, true);
+    hipLaunchKernelGGL((ssd_gram<N>), g0, dim3(kThreads), 0, stream, a);
+    s6_timing_mark("ssd_gram", stream, false);
     dim3 grid(static_cast<unsigned>(a.batch * a.H));
     s6_timing_mark("ssd_chunked", stream, true);
     if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true>), grid, dim3(kThreads), 0, stream, a);

@@ -452,10 +452,7 @@ int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b,
                          chunk_len, workspace, workspace_bytes, stream);
 }
 
-int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
-                const float* A, const float* Dskip, const float* dt_bias, const float* h0,
-                void* y, float* h_last,
-                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype, void* stream) {
+static int ssd_check(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype) {
     if (io_dtype != SSM_BF16)
         return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 io (its products run on bf16 matrix cores)");
     if (N != 64 && N != 128) return fail(SSM_ERR_N, "N = %lld: the SSD layer is built for N = 64 or 128", (long long)N);
@@ -470,13 +467,42 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
     // one batch row's x (or y, z) and B, C are addressed with 32-bit byte offsets
     if (L * H * P * 2 > (int64_t(1) << 31) - 1 || L * N * 2 > (int64_t(1) << 31) - 1)
         return fail(SSM_ERR_SHAPE, "L * H * 64 * 2 bytes exceed 2 GiB per batch row");
+    // one batch row's C . B chunks (L / 64 x 16 KB) are addressed with 32-bit byte offsets too
+    const int64_t nch = (L + 63) / 64;
+    if (nch * 16384 > (int64_t(1) << 31) - 1 || batch * nch > (int64_t(1) << 31) - 1)
+        return fail(SSM_ERR_SHAPE, "L = %lld: the per-chunk C . B workspace of a batch row exceeds 2 GiB",
+                    (long long)L);
+    return 0;
+}
+
+int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype) {
+    const int rc = ssd_check(batch, L, H, P, N, io_dtype);
+    if (rc) return rc;
+    ok();
+    return ssd_gram_bytes(batch, L);
+}
+
+int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                void* y, float* h_last,
+                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
+                void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = ssd_check(batch, L, H, P, N, io_dtype);
+    if (rc) return rc;
+    const int64_t elems = batch * L * H * P;
     struct { const void* p; const char* n; } req[] = {
         {x, "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"}, {dt_bias, "dt_bias"}, {y, "y"}};
     for (auto& r : req)
         if (!r.p) return fail(SSM_ERR_NULL, "%s is NULL", r.n);
     struct { const void* p; int64_t a; const char* n; } al[] = {
         {x, 16, "x"}, {z, 16, "z"}, {y, 16, "y"}, {delta, 2, "delta"}, {B, 16, "B"}, {C, 16, "C"},
-        {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 16, "h0"}, {h_last, 16, "h_last"}};
+        {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 16, "h0"}, {h_last, 16, "h_last"},
+        {workspace, 16, "workspace"}};
+    const int64_t wsb = ssd_gram_bytes(batch, L);
+    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)wsb);
+    if (workspace_bytes < wsb)
+        return fail(SSM_ERR_WORKSPACE, "workspace has %lld bytes; %lld needed", (long long)workspace_bytes,
+                    (long long)wsb);
     for (auto& r : al)
         if (r.p && !aligned(r.p, r.a))
             return fail(SSM_ERR_ALIGN, "%s is not %lld-byte aligned", r.n, (long long)r.a);
@@ -489,7 +515,13 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
         for (auto& i : ins)
             if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
     if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+    const Range wr = rng("workspace", workspace, wsb);
+    for (auto& i : ins)
+        if (overlap(wr, i)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", i.name);
+    for (auto& o : outs)
+        if (overlap(wr, o)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", o.name);
     SsdArgs a{};
+    a.gram = static_cast<float*>(workspace);
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias;
     a.h0 = h0; a.y = y; a.h_last = h_last;
     a.batch = batch; a.L = L; a.H = H; a.N = N;

@@ -277,9 +277,10 @@ def test_ssd_validation():
     L = binding.lib()
     v = ctypes.c_void_p
     base = 1 << 40
-    p = [v(base + i * (1 << 28)) for i in range(11)]
-    # x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last | batch, L, H, P, N, io
-    call = lambda q, P=64, N=128, io=1, H=4: L.ssm_ssd_fwd(*q, 2, 100, H, P, N, io, None)
+    p = [v(base + i * (1 << 28)) for i in range(12)]
+    ws = binding.lib().ssm_ssd_fwd_workspace_bytes(2, 100, 4, 64, 128, 1)
+    # x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last | batch, L, H, P, N, io | workspace, bytes
+    call = lambda q, P=64, N=128, io=1, H=4, nws=ws: L.ssm_ssd_fwd(*q[:11], 2, 100, H, P, N, io, q[11], nws, None)
     assert call(p, io=0) == E_DTYPE                 # bf16 only
     assert call(p, N=96) == E_N and call(p, N=16) == E_N
     assert call(p, P=32) == E_SHAPE
@@ -292,6 +293,27 @@ def test_ssd_validation():
     assert call(q) == E_ALIAS                       # y on top of x
     q = list(p); q[10] = p[8]
     assert call(q) == E_ALIAS                       # h_last on top of h0
+    q = list(p); q[11] = None
+    assert call(q) == E_WS                   # workspace missing
+    assert call(p, nws=ws - 1) == E_WS       # workspace too small
+    q = list(p); q[11] = p[3]
+    assert call(q) == E_ALIAS                       # workspace on top of B
+    q = list(p); q[11] = p[9]
+    assert call(q) == E_ALIAS                       # workspace on top of y
+    q = list(p); q[11] = v(base + 11 * (1 << 28) + 4)
+    assert call(q) == E_ALIGN
+
+
+def test_ssd_workspace_formula():
+    """One 64 x 64 fp32 block of C . B per (batch row, 64-token chunk), ragged chunks rounded up."""
+    f = binding.lib().ssm_ssd_fwd_workspace_bytes
+    for batch, L in ((1, 1), (2, 64), (2, 65), (8, 2048), (3, 1000)):
+        assert f(batch, L, 80, 64, 128, 1) == batch * -(-L // 64) * 64 * 64 * 4
+        assert f(batch, L, 80, 64, 64, 1) == batch * -(-L // 64) * 64 * 64 * 4
+    assert f(1, 100, 4, 64, 96, 1) == E_N
+    assert f(1, 100, 4, 32, 128, 1) == E_SHAPE
+    assert f(1, 100, 4, 64, 128, 0) == E_DTYPE
+    assert f(1, 10_000_000, 1, 64, 64, 1) == E_SHAPE  # a batch row's blocks beyond 32-bit offsets
 
 
 def test_last_error_is_per_thread():
