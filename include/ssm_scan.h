@@ -278,7 +278,7 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  *   h0, h_last (batch, H, 64, N) float32, 16-byte aligned; NULL = zeros / not wanted.
  *   workspace at least ssm_ssd_fwd_workspace_bytes(...) bytes of device
  *             memory, 16-byte aligned, owned by the caller, contents ignored;
- *             it receives C_t . B_i of every chunk (fp32, no head in it), which
+ *             it receives C_t . B_i of every chunk (bf16, no head in it), which
  *             all heads of a batch row share.  It must not overlap any argument
  *             and must not be used by another call until this one's work on
  *             the stream is done.
@@ -294,7 +294,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes ssm_ssd_fwd needs: batch * ceil(L / 64) * 16384.  Negative
+/* Workspace bytes ssm_ssd_fwd needs: batch * ceil(L / 64) * 8192.  Negative
  * ssm_status for an invalid shape.  Host-only; touches no device. */
 int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype);
 

@@ -16,7 +16,7 @@ struct SsdArgs {
     const float* h0;     // (batch, H, 64, N) or NULL
     void* y;             // (batch, L, H, 64) bf16
     float* h_last;       // (batch, H, 64, N) or NULL
-    float* gram;         // workspace: (batch, ceil(L / 64), 64, 64) fp32, C_t . B_i per chunk
+    uint16_t* gram;      // workspace: (batch, ceil(L / 64), 64, 64) bf16, C_t . B_i per chunk
     int64_t batch, L, H, N;
 };
 hipError_t ssd_launch(const SsdArgs& a, hipStream_t stream);

@@ -42,6 +42,7 @@ namespace ssd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;          // tokens per chunk
@@ -87,7 +88,24 @@ struct alignas(16) Smem {
     float S2[kQ];               // S_t * log2(e)
     float Dl[kQ];               // Delta_t
     float Wt[kQ];               // exp(S_end - S_t) Delta_t
+    // Each wavefront's output rows pass through LDS (fp32, 16 rows of 64
+    // channels, row stride kLdY floats) to be stored row by row.  When a row of
+    // St holds 256 bytes the wavefront's own 16 St rows serve (it rewrites them
+    // only afterwards); otherwise a separate area.
+    static constexpr int kLdY = 68;
+    static constexpr bool kYinSt = kLdS * 2 >= kP * 4;
+    float Ys[kYinSt ? 0 : 4][16][kLdY];
 };
+
+template <int N>
+__device__ __forceinline__ float* ystage(Smem<N>& sm, int w) {
+    if constexpr (Smem<N>::kYinSt) {
+        static_assert(Smem<N>::kLdS * 2 == Smem<N>::kLdY * 4, "St rows and staging rows must have the same stride");
+        return reinterpret_cast<float*>(&sm.St[16 * w][0]);
+    } else {
+        return &sm.Ys[w][0][0];
+    }
+}
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
@@ -119,8 +137,9 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 
 // ---------------------------------------------------------------------------
-// ssd_gram: G[t][i] = C_t . B_i (fp32) for every (batch row, chunk), the part
-// of the mixer that no head changes.  Workgroup = (batch row, chunk);
+// ssd_gram: G[t][i] = C_t . B_i for every (batch row, chunk), the part
+// of the mixer that no head changes, accumulated in fp32 and stored as bf16
+// (it only ever enters a bf16 matrix-core operand).  Workgroup = (batch row, chunk);
 // wavefront w computes rows t = 16w .. 16w+15.  Rows past the sequence end
 // read B, C as zero, so their G is zero.
 // ---------------------------------------------------------------------------
@@ -139,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void ssd_gram(SsdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         cop[ks] = __builtin_bit_cast(bf16x8, ld16(rC, ((16 * w + r) * N + 32 * ks + 8 * q) * 2, so));
-    float* g = a.gram + ((b * nch + c) * kQ + 16 * w + r) * kQ;
+    uint16_t* g = a.gram + ((b * nch + c) * kQ + 16 * w + r) * kQ;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
         // A operand: B rows i = 16ib + r; D[m = i][n = t]: lane slot j = G[t = 16w + r][i = 16ib + 4q + j]
@@ -147,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void ssd_gram(SsdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             acc = mfma(__builtin_bit_cast(bf16x8, ld16(rB, ((16 * ib + r) * N + 32 * ks + 8 * q) * 2, so)), cop[ks], acc);
-        *reinterpret_cast<float4*>(g + 16 * ib + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<uint2*>(g + 16 * ib + 4 * q) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
     }
 }
 
@@ -172,54 +191,57 @@ struct StageRegs {
 template <int N>
 __device__ __forceinline__ void load_stage(const SeqIO& io, int t0, int w, StageRegs<N>& r) {
     const int tid = threadIdx.x;
+    // piece k of a thread sits kThreads * k / (row length / 8) rows below piece 0:
+    // one lane offset per tensor, the row step goes to the scalar offset
+    constexpr int kXRows = kThreads / (kP / 8), kBRows = kThreads / (N / 8);
+    const uint32_t vx = (tid / (kP / 8)) * io.xrow + (tid % (kP / 8)) * 16;
+    const uint32_t vb = (tid / (N / 8)) * io.bcrow + (tid % (N / 8)) * 16;
+#pragma unroll
+    for (int k = 0; k < StageRegs<N>::kXSeg; ++k)
+        r.x[k] = ld16(io.x, vx, static_cast<uint32_t>(t0 + kXRows * k) * io.xrow);
+#pragma unroll
+    for (int k = 0; k < StageRegs<N>::kBSeg; ++k)
+        r.b[k] = ld16(io.B, vb, static_cast<uint32_t>(t0 + kBRows * k) * io.bcrow);
     const uint32_t so = static_cast<uint32_t>(t0);
-#pragma unroll
-    for (int k = 0; k < StageRegs<N>::kXSeg; ++k) {
-        const int s = tid + kThreads * k, t = s / (kP / 8), p0 = (s % (kP / 8)) * 8;
-        r.x[k] = ld16(io.x, t * io.xrow + p0 * 2, so * io.xrow);
-    }
-#pragma unroll
-    for (int k = 0; k < StageRegs<N>::kBSeg; ++k) {
-        const int s = tid + kThreads * k, t = s / (N / 8), n0 = (s % (N / 8)) * 8;
-        r.b[k] = ld16(io.B, t * io.bcrow + n0 * 2, so * io.bcrow);
-    }
     if (w == 0)
         r.dl = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(io.dl, (tid & 63) * io.dlrow,
                                                                           so * io.dlrow, 0));
 }
 
 // What wavefront w reads from memory for its own tokens t = 16w + r: C rows
-// (the B operand of the state term), G rows (for M), the gate.
+// (the B operand of the state term), G rows (for M), and the gate of its
+// output rows in row order (lane l: row 8k + l / 8, channels 8 (l % 8) .. +7).
 template <int N>
 struct OwnRegs {
     static constexpr int KS = N / 32;
     bf16x8 c[KS];              // C[t][32ks + 8q .. +7]
-    float4 g[2][2];            // G[t][32ks + 8q .. +7], ks < 1 + (w >= 2)
-    uint2 z[4];                // z[t][16pb + 4q .. +3]
+    uint4 g[2];                // G[t][32ks + 8q .. +7] (bf16), ks < 1 + (w >= 2)
+    uint4 z[2];                // z[16w + 8k + l / 8][8 (l % 8) .. +7]
 };
 
-template <int N, bool GATED>
-__device__ __forceinline__ void load_own(const SeqIO& io, int c, int t0, int w, OwnRegs<N>& o) {
+template <int N>
+__device__ __forceinline__ void load_cg(const SeqIO& io, int c, int t0, int w, OwnRegs<N>& o) {
     const int l = threadIdx.x & 63, r = l & 15, q = l >> 4, t = 16 * w + r;
     const uint32_t so = static_cast<uint32_t>(t0);
 #pragma unroll
     for (int ks = 0; ks < OwnRegs<N>::KS; ++ks)
-        o.c[ks] = __builtin_bit_cast(bf16x8, ld16(io.C, t * io.bcrow + (32 * ks + 8 * q) * 2, so * io.bcrow));
+        o.c[ks] = __builtin_bit_cast(bf16x8, ld16(io.C, t * io.bcrow + 8 * q * 2, so * io.bcrow + 64 * ks));
     const uint32_t gs = static_cast<uint32_t>(c) * io.gchunk;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 0 || w >= 2) {
+    for (int ks = 0; ks < 2; ++ks)
+        if (ks == 0 || w >= 2) o.g[ks] = ld16(io.G, (t * kQ + 8 * q) * 2, gs + 64 * ks);
+}
+
+__device__ __forceinline__ uint32_t row_off(const SeqIO& io, int w) {          // row-order lane offset
+    const int l = threadIdx.x & 63;
+    return (16 * w + (l >> 3)) * io.xrow + (l & 7) * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void load_z(const SeqIO& io, int t0, int w, OwnRegs<N>& o) {
+    const uint32_t v = row_off(io, w);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                o.g[ks][h] = __builtin_bit_cast(float4, ld16(io.G, (t * kQ + 32 * ks + 8 * q + 4 * h) * 4, gs));
-        }
-    }
-    if constexpr (GATED) {
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb)
-            o.z[pb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                   io.z, t * io.xrow + (16 * pb + 4 * q) * 2, so * io.xrow, 0));
-    }
+    for (int k = 0; k < 2; ++k) o.z[k] = ld16(io.z, v, static_cast<uint32_t>(t0 + 8 * k) * io.xrow);
 }
 
 // Stage one chunk: x and B rows into LDS; wavefront 0 scans the step sizes
@@ -303,27 +325,32 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
         io.xrow = static_cast<uint32_t>(a.H * kP * 2);
         io.bcrow = N * 2;
         io.dlrow = static_cast<uint32_t>(a.H * 2);
-        io.gchunk = kQ * kQ * 4;
+        io.gchunk = kQ * kQ * 2;
         io.x = rsrc(static_cast<const uint16_t*>(a.x) + xoff, xbytes);
         io.z = rsrc(a.z ? static_cast<const uint16_t*>(a.z) + xoff : nullptr, a.z ? xbytes : 0);
         io.y = rsrc(static_cast<uint16_t*>(a.y) + xoff, xbytes);
         io.B = rsrc(static_cast<const uint16_t*>(a.B) + b * a.L * N, a.L * N * 2);
         io.C = rsrc(static_cast<const uint16_t*>(a.C) + b * a.L * N, a.L * N * 2);
         io.dl = rsrc(static_cast<const uint16_t*>(a.delta) + b * a.L * a.H + h, ((a.L - 1) * a.H + 1) * 2);
-        io.G = rsrc(a.gram + b * nchunks * kQ * kQ, static_cast<int64_t>(nchunks) * kQ * kQ * 4);
+        io.G = rsrc(a.gram + b * nchunks * kQ * kQ, static_cast<int64_t>(nchunks) * kQ * kQ * 2);
     }
     StageRegs<N> sr;
     OwnRegs<N> own;
     load_stage<N>(io, 0, w, sr);
-    load_own<N, GATED>(io, 0, 0, w, own);
+    load_cg<N>(io, 0, 0, w, own);
+    if constexpr (GATED) load_z<N>(io, 0, w, own);
+    const uint32_t vrow = row_off(io, w);
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * kQ;
         const int nt = static_cast<int>(a.L - t0 < kQ ? a.L - t0 : kQ);
         stage_chunk<N>(sm, sr, nt, A, bias, w);
         __syncthreads();                               // chunk staged, incoming state published
-        const int t1 = t0 + kQ;
-        if (c + 1 < nchunks) load_stage<N>(io, t1, w, sr);
+        // Prefetches are unconditional (the last chunk reloads itself): with no
+        // branch around them the compiler waits on each load by its exact
+        // position in the in-order memory counter instead of draining it.
+        const int cn = c + 1 < nchunks ? c + 1 : c, t1 = cn * kQ;
+        load_stage<N>(io, t1, w, sr);
 
         // M^T as the B operand of y^T: lane (r, q) holds M[t = 16w + r][i = 32ks + 8q .. +7]
         const float s2t = sm.S2[tw];
@@ -338,8 +365,9 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
                 const float4 db = *reinterpret_cast<const float4*>(&sm.Dl[i0 + 4]);
                 const float si[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
                 const float di[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-                const float gi[8] = {own.g[ks][0].x, own.g[ks][0].y, own.g[ks][0].z, own.g[ks][0].w,
-                                     own.g[ks][1].x, own.g[ks][1].y, own.g[ks][1].z, own.g[ks][1].w};
+                const uint4 gw = own.g[ks];
+                const float gi[8] = {lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y),
+                                     lo_bf16(gw.z), hi_bf16(gw.z), lo_bf16(gw.w), hi_bf16(gw.w)};
                 float m[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -349,8 +377,9 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
         }
         const float e = __builtin_amdgcn_exp2f(s2t);
 
-        // y^T for this wavefront's tokens and every channel block:
-        //     lane slot j = y[t = 16w + r][p = 16pb + 4q + j]
+        // y^T before the gate for this wavefront's tokens and every channel
+        // block: lane slot j = y[t = 16w + r][p = 16pb + 4q + j]
+        f32x4 yp[4];
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
             f32x4 yi = f32x4{0.f, 0.f, 0.f, 0.f}, ys = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -361,20 +390,11 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
             for (int ks = 0; ks < KS; ++ks)
                 ys = mfma(lds8(&sm.St[16 * pb + r][32 * ks + 8 * q]), own.c[ks], ys);
             const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xs[tw][16 * pb + 4 * q]);
-            float yv[4] = {yi[0] + e * ys[0] + Dd * lo_bf16(xv.x), yi[1] + e * ys[1] + Dd * hi_bf16(xv.x),
+            yp[pb] = f32x4{yi[0] + e * ys[0] + Dd * lo_bf16(xv.x), yi[1] + e * ys[1] + Dd * hi_bf16(xv.x),
                            yi[2] + e * ys[2] + Dd * lo_bf16(xv.y), yi[3] + e * ys[3] + Dd * hi_bf16(xv.y)};
-            if constexpr (GATED) {
-                yv[0] *= s6::silu(lo_bf16(own.z[pb].x));
-                yv[1] *= s6::silu(hi_bf16(own.z[pb].x));
-                yv[2] *= s6::silu(lo_bf16(own.z[pb].y));
-                yv[3] *= s6::silu(hi_bf16(own.z[pb].y));
-            }
-            // rows past the sequence end: stored through the bounded buffer, i.e. dropped
-            const uint2 o = make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, o), io.y, tw * io.xrow + (16 * pb + 4 * q) * 2,
-                                                  static_cast<uint32_t>(t0) * io.xrow, 0);
         }
-        if (c + 1 < nchunks) load_own<N, GATED>(io, c + 1, t1, w, own);
+        // C and G of the next chunk (their registers are free now)
+        load_cg<N>(io, cn, t1, w, own);
 
         // --- state update: state^T = exp(S_end) state^T + B^T (W x), W_i = exp(S_end - S_i) Delta_i
         const float dec = __builtin_amdgcn_exp2f(sm.S2[kQ - 1]);
@@ -399,7 +419,35 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
             st[nb] = sv;
         }
         __syncthreads();                               // every read of St, Xs, Bs of this chunk is done
-        publish_state<N>(sm, st, w);
+
+        // --- outputs in row order through this wavefront's staging rows, gate, store
+        float* ysm = ystage<N>(sm, w);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+            *reinterpret_cast<float4*>(ysm + r * Smem<N>::kLdY + 16 * pb + 4 * q) =
+                make_float4(yp[pb][0], yp[pb][1], yp[pb][2], yp[pb][3]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float* src = ysm + (8 * k + (l >> 3)) * Smem<N>::kLdY + 8 * (l & 7);
+            const float4 u0 = *reinterpret_cast<const float4*>(src);
+            const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+            float yv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            if constexpr (GATED) {
+                const uint32_t zw[4] = {own.z[k].x, own.z[k].y, own.z[k].z, own.z[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    yv[2 * j] *= s6::silu(lo_bf16(zw[j]));
+                    yv[2 * j + 1] *= s6::silu(hi_bf16(zw[j]));
+                }
+            }
+            // rows past the sequence end: stored through the bounded buffer, i.e. dropped
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(v4u, make_uint4(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]), pack2(yv[4], yv[5]),
+                                                   pack2(yv[6], yv[7]))),
+                io.y, vrow, static_cast<uint32_t>(t0 + 8 * k) * io.xrow, 0);
+        }
+        if constexpr (GATED) load_z<N>(io, t1, w, own);
+        publish_state<N>(sm, st, w);                   // after this wavefront's staging reads (same rows)
     }
     if (a.h_last) {
         float* hl = a.h_last + (b * a.H + h) * kP * N;
@@ -414,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
 
 using namespace ssd;
 
-int64_t ssd_gram_bytes(int64_t batch, int64_t L) { return batch * ((L + kQ - 1) / kQ) * kQ * kQ * 4; }
+int64_t ssd_gram_bytes(int64_t batch, int64_t L) { return batch * ((L + kQ - 1) / kQ) * kQ * kQ * 2; }
 
 template <int N>
 static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {

@@ -467,9 +467,9 @@ static int ssd_check(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, 
     // one batch row's x (or y, z) and B, C are addressed with 32-bit byte offsets
     if (L * H * P * 2 > (int64_t(1) << 31) - 1 || L * N * 2 > (int64_t(1) << 31) - 1)
         return fail(SSM_ERR_SHAPE, "L * H * 64 * 2 bytes exceed 2 GiB per batch row");
-    // one batch row's C . B chunks (L / 64 x 16 KB) are addressed with 32-bit byte offsets too
+    // one batch row's C . B chunks (L / 64 x 8 KB) are addressed with 32-bit byte offsets too
     const int64_t nch = (L + 63) / 64;
-    if (nch * 16384 > (int64_t(1) << 31) - 1 || batch * nch > (int64_t(1) << 31) - 1)
+    if (nch * 8192 > (int64_t(1) << 31) - 1 || batch * nch > (int64_t(1) << 31) - 1)
         return fail(SSM_ERR_SHAPE, "L = %lld: the per-chunk C . B workspace of a batch row exceeds 2 GiB",
                     (long long)L);
     return 0;
@@ -521,7 +521,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
     for (auto& o : outs)
         if (overlap(wr, o)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", o.name);
     SsdArgs a{};
-    a.gram = static_cast<float*>(workspace);
+    a.gram = static_cast<uint16_t*>(workspace);
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias;
     a.h0 = h0; a.y = y; a.h_last = h_last;
     a.batch = batch; a.L = L; a.H = H; a.N = N;

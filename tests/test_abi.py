@@ -305,15 +305,15 @@ def test_ssd_validation():
 
 
 def test_ssd_workspace_formula():
-    """One 64 x 64 fp32 block of C . B per (batch row, 64-token chunk), ragged chunks rounded up."""
+    """One 64 x 64 bf16 block of C . B per (batch row, 64-token chunk), ragged chunks rounded up."""
     f = binding.lib().ssm_ssd_fwd_workspace_bytes
     for batch, L in ((1, 1), (2, 64), (2, 65), (8, 2048), (3, 1000)):
-        assert f(batch, L, 80, 64, 128, 1) == batch * -(-L // 64) * 64 * 64 * 4
-        assert f(batch, L, 80, 64, 64, 1) == batch * -(-L // 64) * 64 * 64 * 4
+        assert f(batch, L, 80, 64, 128, 1) == batch * -(-L // 64) * 64 * 64 * 2
+        assert f(batch, L, 80, 64, 64, 1) == batch * -(-L // 64) * 64 * 64 * 2
     assert f(1, 100, 4, 64, 96, 1) == E_N
     assert f(1, 100, 4, 32, 128, 1) == E_SHAPE
     assert f(1, 100, 4, 64, 128, 0) == E_DTYPE
-    assert f(1, 10_000_000, 1, 64, 64, 1) == E_SHAPE  # a batch row's blocks beyond 32-bit offsets
+    assert f(1, 20_000_000, 1, 64, 64, 1) == E_SHAPE  # a batch row's blocks beyond 32-bit offsets
 
 
 def test_last_error_is_per_thread():
