@@ -135,7 +135,7 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
         t = {}
     rec = {}
     for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_bwd_carries",
-                  "s6_carry_scan2", "s6_chunk_bwd", "s6_bwd_reduce", "ssd_chunked"):
+                  "s6_carry_scan2", "s6_chunk_bwd", "s6_bwd_reduce", "ssd_gram", "ssd_chunked"):
         try:
             fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
         except SystemExit:
@@ -344,10 +344,11 @@ def ssd_bytes(batch, L, H, P, N, gated=True):
 
 
 def ssd_flops(batch, L, H, P, N, Q=64):
-    """Chunked evaluation: C B^T once per (batch row, chunk); per head and chunk the causal half of the
-    masked Q x Q x P product, the state term Q x N x P and the state update P x Q x N (2 flops per MAC)."""
+    """Matrix-core work of ssd_chunked: per head and chunk the causal half of the masked Q x Q x P
+    product, the state term Q x N x P and the state update P x Q x N (2 flops per MAC).  C B^T, once per
+    (batch row, chunk), is ssd_gram's (2 Q Q N per chunk) and not counted here."""
     chunks = -(-L // Q)
-    return batch * chunks * (2 * Q * Q * N + H * (Q * Q * P + 2 * Q * N * P + 2 * P * Q * N))
+    return batch * chunks * H * (Q * Q * P + 2 * Q * N * P + 2 * P * Q * N)
 
 
 def bench_ssd(args):
@@ -363,9 +364,10 @@ def bench_ssd(args):
     x, dl, z, B, C = (bf(a) for a in (s.x, s.delta, s.z, s.B, s.C))
     A, Dk, bias = f32(s.A), f32(s.Dskip), f32(s.dt_bias)
     y = torch.empty_like(x)
+    ws = torch.empty(binding.ssd_workspace_bytes(batch, L, H, N, P), dtype=torch.uint8, device=dev)
 
     def step():
-        binding.ssd_fwd(x, dl, A, B, C, Dk, bias, z=z, out=y, return_last_state=False)
+        binding.ssd_fwd(x, dl, A, B, C, Dk, bias, z=z, out=y, return_last_state=False, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -388,6 +390,10 @@ def bench_ssd(args):
     binding.timing_enable(False)
     c, kms = binding.timing_collect()["ssd_chunked"]
     avg_ms = kms / c
+    binding.timing_enable(True)
+    timed(args.steps)
+    binding.timing_enable(False)
+    breakdown = {k: {"launches": n, "avg_ms": round(t / n, 5)} for k, (n, t) in binding.timing_collect().items()}
     E = batch * L * H * P
     abytes = ssd_bytes(batch, L, H, P, N)
     flops = ssd_flops(batch, L, H, P, N)
@@ -404,7 +410,8 @@ def bench_ssd(args):
                         "kernel": "ssd_chunked", "avg_launch_ms": round(avg_ms, 5),
                         "work": f"{abytes} algorithmic bytes per launch (x, z read, y written, delta, B, C)"},
            "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": PEAK_BF16_TFLOPS,
-                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops}}
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops},
+           "kernels": breakdown}
     print(json.dumps(out), flush=True)
 
 
