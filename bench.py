@@ -150,6 +150,35 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
     print(json.dumps(t[workload]))
 
 
+FLUSH_BYTES = 1 << 30          # four times the 256 MB Infinity Cache (MALL)
+
+
+def flushed_timing(step, stream, algorithmic_bytes, elements, reps=30):
+    """Single steps with the MALL (and L2) flushed by an untimed 1 GiB device write before each one:
+    median, p10 and p90 over `reps` repetitions (events on the step's stream), and the HBM fraction of
+    the algorithmic bytes at the median.  This is the pure-HBM figure; `value` above is the hot loop."""
+    import torch
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=stream.device)
+    ev = []
+    torch.cuda.synchronize()
+    for i in range(reps):
+        buf.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: ms[min(len(ms) - 1, int(round(f * (len(ms) - 1))))]
+    med = q(0.5)
+    gbps = algorithmic_bytes / (med * 1e-3) / 1e9
+    del buf
+    return {"reps": reps, "flush_bytes": FLUSH_BYTES, "median_ms": round(med, 5), "p10_ms": round(q(0.1), 5),
+            "p90_ms": round(q(0.9), 5), "elements_per_s": round(elements / (med * 1e-3), 1),
+            "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def cpu_baseline(s, min_seconds=10.0, max_passes=12):
     """The float64 oracle as it stands, on the host, over whole passes of the workload."""
     import numpy as np
@@ -250,7 +279,8 @@ def bench_decode(args):
                         "traffic": measured_traffic(args.workload, "s6_step"), "kernel": "s6_step",
                         "avg_launch_ms": round(avg_ms, 5),
                         "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters"
-                                + (", + the conv state read and written" if conv else "") + ")"}}
+                                + (", + the conv state read and written" if conv else "") + ")"},
+           "mall_flushed": flushed_timing(step, stream, abytes, batch * D)}
     print(json.dumps(out), flush=True)
 
 
@@ -334,7 +364,8 @@ def bench_bwd(args, k):
                         "avg_launch_ms": round(avg_ms, 5),
                         "work": f"{BWD_SLOTS_PER_ELEMENT} fp32 VALU slots (= {2 * BWD_SLOTS_PER_ELEMENT} "
                                 f"FMA-equivalent flops) per element x {E} elements per launch"},
-           "kernels": kernels}
+           "kernels": kernels,
+           "mall_flushed": flushed_timing(step, stream, abytes, E)}
     print(json.dumps(out), flush=True)
 
 
@@ -411,7 +442,8 @@ def bench_ssd(args):
                         "work": f"{abytes} algorithmic bytes per launch (x, z read, y written, delta, B, C)"},
            "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": PEAK_BF16_TFLOPS,
                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops},
-           "kernels": breakdown}
+           "kernels": breakdown,
+           "mall_flushed": flushed_timing(step, stream, abytes, E)}
     print(json.dumps(out), flush=True)
 
 
@@ -546,7 +578,8 @@ def main():
                       "chunk_len": chunk_len, "n_chunks": n_chunks, **({"conv_k": CONV_K} if conv else {})},
            "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
                    "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes},
-           "roofline": roofline, "kernels": kernels}
+           "roofline": roofline, "kernels": kernels,
+           "mall_flushed": flushed_timing(step, stream, abytes, E)}
     if not args.no_cpu_baseline and not conv:
         out["cpu_baseline"] = cpu_baseline(s)
     print(json.dumps(out), flush=True)

@@ -316,10 +316,34 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
 // channel) are read and written as whole 16-byte vectors by consecutive lanes.
 constexpr int kStepRows = 8;      // batch rows per workgroup (A is loaded once for them)
 
+// Four consecutive io elements (a lane's four B or C entries), loaded as one
+// vector when the tensor is aligned for it (VEC), else element by element, and
+// widened on use.
+template <class IO, bool VEC> struct Quad;
+template <bool VEC> struct Quad<F32, VEC> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (VEC) v = *reinterpret_cast<const float4*>(p);
+        else v = make_float4(p[0], p[1], p[2], p[3]);
+    }
+    __device__ __forceinline__ float get(int j) const { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+};
+template <bool VEC> struct Quad<BF16, VEC> {
+    uint2 v;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        if constexpr (VEC) v = *reinterpret_cast<const uint2*>(p);
+        else v = make_uint2(p[0] | (static_cast<uint32_t>(p[1]) << 16), p[2] | (static_cast<uint32_t>(p[3]) << 16));
+    }
+    __device__ __forceinline__ float get(int j) const {
+        const uint32_t w = j < 2 ? v.x : v.y;
+        return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
 // With the local convolution (K > 0) the step input is silu(b + w . [conv
 // state, xin]); the four lanes of a channel compute it redundantly and the
 // first one shifts the conv state in place.
-template <class IO, bool GATED, int K>
+template <class IO, bool GATED, int K, bool VEC>
 __global__ __launch_bounds__(kBlock) void s6_step(S6StepArgs a) {
     using T = typename IO::T;
     const int q = threadIdx.x & 3;
@@ -347,46 +371,63 @@ __global__ __launch_bounds__(kBlock) void s6_step(S6StepArgs a) {
     }
     T* CS = static_cast<T*>(a.conv_state);
 
+    // Every load of the workgroup's rows is issued before the first store, so
+    // the rows' memory latencies overlap (the compiler would not move a later
+    // row's loads above an earlier row's stores: it cannot see that they never
+    // alias).  Rows past the batch end load the last row and are not stored.
     const int64_t b_begin = static_cast<int64_t>(blockIdx.y) * kStepRows;
-    const int64_t b_end = (b_begin + kStepRows < a.batch) ? b_begin + kStepRows : a.batch;
-    for (int64_t b = b_begin; b < b_end; ++b) {
-        const int64_t bd = b * a.D + d;
+    float4 hv[kStepRows];
+    T xr[kStepRows], dr[kStepRows], zr[kStepRows];
+    Quad<IO, VEC> br[kStepRows], cr[kStepRows];
+    T wr[kStepRows][K > 1 ? K - 1 : 1];
+#pragma unroll
+    for (int r = 0; r < kStepRows; ++r) {
+        const int64_t b = b_begin + r < a.batch ? b_begin + r : a.batch - 1;
         const int64_t brow = b * a.D;
-        float xv = IO::load(X + brow, dd);
+        xr[r] = X[brow + dd];
+        dr[r] = DL[brow + dd];
+        if (GATED) zr[r] = Z[brow + dd];
+        br[r].load(Bm + b * kN + 4 * q);
+        cr[r].load(Cm + b * kN + 4 * q);
+        hv[r] = reinterpret_cast<const float4*>(a.h + (b * a.D + d) * kN)[q];   // d is clamped: always in bounds
+        if constexpr (K > 1) {
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) wr[r][i] = CS[(b * (K - 1) + i) * a.D + dd];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kStepRows; ++r) {
+        const int64_t b = b_begin + r;
+        if (b >= a.batch) break;                       // uniform over the workgroup
+        const int64_t brow = b * a.D;
+        float xv = IO::load(&xr[r], 0);
         if constexpr (K > 0) {
-            float win[K > 1 ? K - 1 : 1];
             float v = cb;
 #pragma unroll
-            for (int i = 0; i < K - 1; ++i) {
-                win[i] = IO::load(CS + (b * (K - 1) + i) * a.D, dd);
-                v = fmaf(cw[i], win[i], v);
-            }
+            for (int i = 0; i < K - 1; ++i) v = fmaf(cw[i], IO::load(&wr[r][i], 0), v);
             v = fmaf(cw[K - 1], xv, v);
             if (active && q == 0) {
 #pragma unroll
-                for (int i = 0; i + 1 < K - 1; ++i) IO::store(CS + (b * (K - 1) + i) * a.D, dd, win[i + 1]);
-                if constexpr (K > 1) IO::store(CS + (b * (K - 1) + K - 2) * a.D, dd, xv);
+                for (int i = 0; i + 1 < K - 1; ++i) CS[(b * (K - 1) + i) * a.D + dd] = wr[r][i + 1];
+                if constexpr (K > 1) CS[(b * (K - 1) + K - 2) * a.D + dd] = xr[r];
             }
             xv = silu(v);
         }
-        const float dt = softplus(IO::load(DL + brow, dd) + bias);
+        const float dt = softplus(IO::load(&dr[r], 0) + bias);
         const float dx = dt * xv;
-        float4* hp = reinterpret_cast<float4*>(a.h + bd * kN) + q;
-        float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (active) hv = *hp;
-        float hs[4] = {hv.x, hv.y, hv.z, hv.w};
+        float hs[4] = {hv[r].x, hv[r].y, hv[r].z, hv[r].w};
         float p = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float dA = __builtin_amdgcn_exp2f(dt * A2[j]);
-            hs[j] = fmaf(dA, hs[j], dx * IO::load(Bm + b * kN, 4 * q + j));
-            p = fmaf(IO::load(Cm + b * kN, 4 * q + j), hs[j], p);
+            hs[j] = fmaf(dA, hs[j], dx * br[r].get(j));
+            p = fmaf(cr[r].get(j), hs[j], p);
         }
-        if (active) *hp = make_float4(hs[0], hs[1], hs[2], hs[3]);
+        if (active) reinterpret_cast<float4*>(a.h + (b * a.D + d) * kN)[q] = make_float4(hs[0], hs[1], hs[2], hs[3]);
         p += __shfl_xor(p, 1, 4);
         p += __shfl_xor(p, 2, 4);
         float yv = fmaf(Dd, xv, p);
-        if (GATED) yv *= silu(IO::load(Z + brow, dd));
+        if (GATED) yv *= silu(IO::load(&zr[r], 0));
         if (active && q == 0) IO::store(Y + brow, dd, yv);
     }
 }
@@ -465,8 +506,12 @@ template <class IO, bool GATED, int K>
 static hipError_t launch_step_t(const S6StepArgs& a, hipStream_t stream) {
     dim3 g(static_cast<unsigned>((a.D + kBlock / 4 - 1) / (kBlock / 4)),
            static_cast<unsigned>((a.batch + kStepRows - 1) / kStepRows));
+    // B and C rows are 16 elements: with 4-element alignment at the base every lane's quad is aligned
+    const uintptr_t qa = 4 * sizeof(typename IO::T) - 1;
+    const bool vec = ((reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C)) & qa) == 0;
     s6_timing_mark("s6_step", stream, true);
-    hipLaunchKernelGGL((s6_step<IO, GATED, K>), g, dim3(kBlock), 0, stream, a);
+    if (vec) hipLaunchKernelGGL((s6_step<IO, GATED, K, true>), g, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((s6_step<IO, GATED, K, false>), g, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_step", stream, false);
     return hipGetLastError();
 }
