@@ -172,6 +172,37 @@ def test_decode_shapes(batch, D, io, gated):
     assert_close(host64(h), rh, TOL[io], f"decode {batch}x{D} h")
 
 
+@pytest.mark.parametrize("io,gated", [("bf16", True), ("f32", False)])
+def test_decode_unaligned_bc_uses_element_loads(io, gated):
+    """B and C one element into their buffers (aligned for their element, not for a 4-element
+    vector) take the element-by-element path of the decode step and give the same result as the
+    oracle; the aligned copies (vector path) agree with it bit for bit."""
+    batch, D = 11, 200
+    A, Dskip, dt_bias, h0 = inputs.decode_params(batch, D)
+    tok = inputs.decode_token(5, batch, D, io=io, gated=gated)
+
+    def shifted(a):
+        pad = np.zeros(1, np.uint16 if io == "bf16" else np.float32)
+        flat = dev(np.concatenate([pad, np.ascontiguousarray(a).reshape(-1)]), io)
+        return flat[1:].view(a.shape)
+
+    B1, C1 = shifted(tok.B), shifted(tok.C)
+    esz = 2 if io == "bf16" else 4
+    assert B1.data_ptr() % (4 * esz) != 0 and C1.data_ptr() % (4 * esz) != 0
+    args = (dev(tok.x, io), dev(tok.delta, io), f32dev(A))
+    rest = (f32dev(Dskip), f32dev(dt_bias))
+    z = dev(tok.z, io) if gated else None
+    h_u, h_a = f32dev(h0), f32dev(h0)
+    y_u = binding.state_update(h_u, *args, B1, C1, *rest, z=z)
+    y_a = binding.state_update(h_a, *args, dev(tok.B, io), dev(tok.C, io), *rest, z=z)
+    torch.cuda.synchronize()
+    ry, rh = oracle.state_update(h0, tok.x, tok.delta, A, tok.B, tok.C, Dskip, dt_bias,
+                                 z=tok.z if gated else None, io=io)
+    assert_close(host64(y_u), ry, TOL[io], "unaligned B, C decode y")
+    assert_close(host64(h_u), rh, TOL[io], "unaligned B, C decode h")
+    assert torch.equal(y_u, y_a) and torch.equal(h_u, h_a)
+
+
 def test_errors_raise_before_launch():
     s = inputs.make_scan_inputs(1, 64, 64, io="bf16", seed=(39, 2009))
     t = _dev_all(s)

@@ -65,3 +65,32 @@ def test_ssd_errors():
     with pytest.raises(binding.SSMError) as e:
         gpu_ssd(s)
     assert e.value.status == -3
+
+
+def test_ssd_workspace_reused_and_checked():
+    """One caller workspace serves a long call and then a shorter one (stale blocks from the first call
+    are overwritten, not read); a workspace one byte short is rejected before any launch."""
+    from gpu_util import dev, f32dev
+    io = "bf16"
+    s1 = inputs.make_ssd_inputs(2, 700, 3, seed=(39, 6400), with_h0=True)
+    s2 = inputs.make_ssd_inputs(1, 130, 3, seed=(39, 6401), with_h0=True)
+    n1 = binding.ssd_workspace_bytes(2, 700, 3, 128)
+    assert n1 == 2 * 11 * 64 * 64 * 2 and binding.ssd_workspace_bytes(1, 130, 3, 128) < n1
+    ws = torch.empty(n1, dtype=torch.uint8, device="cuda")
+
+    def run(s, w):
+        return binding.ssd_fwd(dev(s.x, io), dev(s.delta, io), f32dev(s.A), dev(s.B, io), dev(s.C, io),
+                               f32dev(s.Dskip), f32dev(s.dt_bias), z=dev(s.z, io), h0=f32dev(s.h0), workspace=w)
+
+    y1, h1 = run(s1, ws)
+    y2, h2 = run(s2, ws)
+    y2f, h2f = run(s2, None)                       # a fresh workspace of its own
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y2f) and torch.equal(h2, h2f)
+    ry1, rh1 = oracle_ssd(s1)
+    assert_close(host64(y1), ry1, TOL["bf16"], "ssd first call y")
+    ry2, rh2 = oracle_ssd(s2)
+    assert_close(host64(y2), ry2, TOL["bf16"], "ssd second call y")
+    small = torch.empty(binding.ssd_workspace_bytes(1, 130, 3, 128) - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        run(s2, small)
