@@ -207,13 +207,20 @@ __device__ __forceinline__ void ckpt_body(const S6BwdArgs& a, int64_t bid) {
 
 // The checkpoint pass (HBM-bound: it writes the checkpoints) and the adjoint
 // carry pass (VALU-bound) are independent: one launch runs both, so they
-// overlap on the chip.  Workgroups [0, nblk * n) take the first job.
+// overlap on the chip.  Workgroups are dispatched in index order, so the two
+// jobs alternate in runs of kXcds (one workgroup of each per XCD) and are
+// resident together; a job's unit u keeps u % kXcds = blockIdx.x % kXcds, the
+// XCD its chunk mapping expects.
 template <class LD, bool GATED>
 __global__ __launch_bounds__(kBlock) void s6_bwd_carries(S6BwdArgs a) {
-    const int64_t first = (a.D + kBlock - 1) / kBlock * a.batch * a.n_chunks;
-    const int64_t i = blockIdx.x;
-    if (i < first) ckpt_body<LD>(a, i);
-    else carry_rev_body<LD, GATED>(a, i - first);
+    const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
+    const int64_t i = blockIdx.x, r = i % (2 * kXcds);
+    const int64_t u = i / (2 * kXcds) * kXcds + r % kXcds;
+    if (r < kXcds) {
+        if (u < nblk * a.n_chunks) ckpt_body<LD>(a, u);
+    } else {
+        if (u < nblk * (a.n_chunks - 1)) carry_rev_body<LD, GATED>(a, u);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -593,7 +600,7 @@ using namespace s6;
 template <class LD, bool GATED>
 static hipError_t launch_bwd_t(const S6BwdArgs& a, hipStream_t stream) {
     const int64_t nblk = (a.D + kBlock - 1) / kBlock * a.batch;
-    dim3 g0(static_cast<unsigned>(nblk * a.n_chunks + (a.n_chunks > 1 ? nblk * (a.n_chunks - 1) : 0)));
+    dim3 g0(static_cast<unsigned>((nblk * a.n_chunks + kXcds - 1) / kXcds * 2 * kXcds));
     s6_timing_mark("s6_bwd_carries", stream, true);
     hipLaunchKernelGGL((s6_bwd_carries<LD, GATED>), g0, dim3(kBlock), 0, stream, a);
     s6_timing_mark("s6_bwd_carries", stream, false);
