@@ -340,6 +340,11 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
     // by exp(A * sum Delta) over the sub-chunks before it.  The chunk's starting
     // state waits in LDS (four values per 16-byte slot, lanes contiguous).
     __shared__ float4 hst_lds[kBlock / kWave][kN / 4][kWave];
+    // The decays Abar of the sub-chunk's tokens, from the recompute pass to the
+    // adjoint pass (registers are full; recomputing them costs 2 VALU per state
+    // and token, LDS a write and a read per four states).  64 KB: with the
+    // starting states, two workgroups fill a CU's 160 KB.
+    __shared__ float4 abar_lds[kBlock / kWave][SUB][kN / 4][kWave];
     const int wv = static_cast<int>(threadIdx.x) >> 6, ln = static_cast<int>(threadIdx.x) & (kWave - 1);
 #pragma unroll
     for (int k = 0; k < kN / 4; ++k) hst_lds[wv][k][ln] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
@@ -441,9 +446,16 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
                 sgs[i] = sg;
                 float yv = Dd * xv;
 #pragma unroll
-                for (int n = 0; n < kN; ++n) {
-                    h[n] = fmaf(__builtin_amdgcn_exp2f(dt * A2[n]), h[n], u * Bv.get(n));
-                    if (GATED) yv = fmaf(Cv.get(n), h[n], yv);
+                for (int k = 0; k < kN / 4; ++k) {
+                    float ab[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int n = 4 * k + m;
+                        ab[m] = __builtin_amdgcn_exp2f(dt * A2[n]);
+                        h[n] = fmaf(ab[m], h[n], u * Bv.get(n));
+                        if (GATED) yv = fmaf(Cv.get(n), h[n], yv);
+                    }
+                    abar_lds[wv][i][k][ln] = make_float4(ab[0], ab[1], ab[2], ab[3]);
                 }
                 float gv = ld.widen(rg[i]);
                 if (GATED) {
@@ -479,8 +491,13 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
                 const RowBC<IO>& Bv = bq[i & 1];
                 const RowBC<IO>& Cv = cq[i & 1];
                 const float dy = dys[i];
-                float dt = dts[i];
-                asm volatile("" : "+v"(dt));     // recompute Abar here rather than keep 16 per token live
+                const float dt = dts[i];
+                float abar[kN];
+#pragma unroll
+                for (int k = 0; k < kN / 4; ++k) {
+                    const float4 v = abar_lds[wv][i][k][ln];     // written by this lane: no barrier needed
+                    abar[4 * k] = v.x; abar[4 * k + 1] = v.y; abar[4 * k + 2] = v.z; abar[4 * k + 3] = v.w;
+                }
                 const float u = dt * xs[i];
                 // the dB / dC terms of lanes that only duplicate channel D-1 must add nothing
                 const float uk = g.active ? u : 0.0f;
@@ -493,7 +510,7 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
                     const float mu = fmaf(Cv.get(n), dy, rho[n]);
                     du = fmaf(mu, Bv.get(n), du);
                     pc[n] = dyk * ht;
-                    const float q = __builtin_amdgcn_exp2f(dt * A2[n]) * mu;
+                    const float q = abar[n] * mu;
                     const float w = q * hs[i][n];
                     sw = fmaf(w, A2[n], sw);
                     dA[n] = fmaf(w, dt, dA[n]);
