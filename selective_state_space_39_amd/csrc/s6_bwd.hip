@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
     const int64_t nsub_max = a.chunk_len / SUB;
     const float* ck = a.ckpt + ((static_cast<int64_t>(g.b) * a.n_chunks + g.c) * nsub_max * (kN + 1)) * D + g.d;
 
-    float A2[kN], h[kN];
+    float A2[kN], hc[kN];      // hc: the chunk's starting state
 #pragma unroll
     for (int n = 0; n < kN; ++n) A2[n] = a.A[g.d * kN + n] * kLog2e;
     const float bias = a.dt_bias[g.d];
@@ -326,13 +326,13 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
     if (g.c > 0) {
         const int64_t cs = static_cast<int64_t>(g.b) * (a.n_chunks - 1) + g.c - 1;
 #pragma unroll
-        for (int n = 0; n < kN; ++n) h[n] = a.carry_H[(cs * kN + n) * D + g.d];
+        for (int n = 0; n < kN; ++n) hc[n] = a.carry_H[(cs * kN + n) * D + g.d];
     } else if (a.h0) {
 #pragma unroll
-        for (int n = 0; n < kN; ++n) h[n] = a.h0[bd * kN + n];
+        for (int n = 0; n < kN; ++n) hc[n] = a.h0[bd * kN + n];
     } else {
 #pragma unroll
-        for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+        for (int n = 0; n < kN; ++n) hc[n] = 0.0f;
     }
 
     // The true state at the start of sub-chunk j >= 1 is its local state (from a
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
     __shared__ float4 abar_lds[kBlock / kWave][SUB][kN / 4][kWave];
     const int wv = static_cast<int>(threadIdx.x) >> 6, ln = static_cast<int>(threadIdx.x) & (kWave - 1);
 #pragma unroll
-    for (int k = 0; k < kN / 4; ++k) hst_lds[wv][k][ln] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+    for (int k = 0; k < kN / 4; ++k) hst_lds[wv][k][ln] = make_float4(hc[4 * k], hc[4 * k + 1], hc[4 * k + 2], hc[4 * k + 3]);
     // Checkpoint j's 17 values are loaded one sub-chunk ahead (raw) and combined
     // with the starting state only when needed, so the load latency is hidden.
     auto ck_load = [&](int j, float (&loc)[kN], float& sl) {
@@ -368,12 +368,13 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
             }
         }
     };
-    auto sub_start = [&](int j, float (&out)[kN]) {
-        float loc[kN], sl = 0.0f;
-        if (j > 0) ck_load(j, loc, sl);
-        ck_combine(j, loc, sl, out);
-    };
-    sub_start(nsub - 1, h);
+    // the checkpoint of the last sub-chunk; each iteration below combines the
+    // pending one into a fresh starting state (no state is carried across
+    // iterations in registers, so the recompute needs no copies of it)
+    float hn[kN], sn = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) hn[n] = 0.0f;
+    if (nsub > 1) ck_load(nsub - 1, hn, sn);
 
     // 2. sub-chunks from the last to the first
     float rho[kN], dA[kN];
@@ -410,10 +411,10 @@ __global__ __launch_bounds__(kBlock, 2) void s6_chunk_bwd(S6BwdArgs a) {
         }
     };
     issue((nsub - 1) * SUB);
-    float hn[kN], sn = 0.0f;
     for (int j = nsub - 1; j >= 0; --j) {
         const int t0 = j * SUB;
-        if (j < nsub - 1) ck_combine(j, hn, sn, h);
+        float h[kN];
+        ck_combine(j, hn, sn, h);
         // recompute: states before each token, step sizes, dy (and dz)
         float hs[SUB][kN];
         float xs[SUB], dts[SUB], sgs[SUB], dys[SUB];
