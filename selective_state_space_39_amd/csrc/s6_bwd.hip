@@ -26,7 +26,8 @@
 //      reverse fold from dh_last (incoming adjoint per chunk) in one grid;
 //   3. s6_chunk_bwd: per chunk, sub-chunk by sub-chunk from the end, the
 //      sub-chunk's starting state is rebuilt from its checkpoint, its states are
-//      recomputed into registers and the adjoint runs back through them;
+//      recomputed into registers (their decays set aside in LDS) and the
+//      adjoint runs back through them;
 //   4. s6_bwd_reduce: deterministic sums of the per-wavefront dB, dC and the
 //      per-chunk dA, dDskip, ddt_bias partials, one grid for both.
 
