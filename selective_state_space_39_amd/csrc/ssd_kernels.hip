@@ -41,7 +41,6 @@
 namespace ssd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -50,9 +49,6 @@ constexpr int kP = 64;          // channels per head
 constexpr int kThreads = 256;   // 4 wavefronts
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ uint16_t to_bf16(float v) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));      // round to nearest even
-}
 __device__ __forceinline__ float from_bf16(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
