@@ -273,7 +273,7 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  *
  *   x, z, y   (batch, L, H, 64) bf16, 16-byte aligned; z NULL = ungated.
  *   delta     (batch, L, H) bf16.
- *   B, C      (batch, L, N) bf16, N = 64 or 128, 16-byte aligned.
+ *   B, C      (batch, L, N) bf16, N = 64, 128 or 256, 16-byte aligned.
  *   A, Dskip, dt_bias (H) float32.
  *   h0, h_last (batch, H, 64, N) float32, 16-byte aligned; NULL = zeros / not wanted.
  *   workspace at least ssm_ssd_fwd_workspace_bytes(...) bytes of device
@@ -282,8 +282,8 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  *             all heads of a batch row share.  It must not overlap any argument
  *             and must not be used by another call until this one's work on
  *             the stream is done.
- * io_dtype must be SSM_BF16 (SSM_ERR_DTYPE otherwise); N other than 64 or
- * 128 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE; a missing or small
+ * io_dtype must be SSM_BF16 (SSM_ERR_DTYPE otherwise); N other than 64, 128
+ * or 256 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE; a missing or small
  * workspace is SSM_ERR_WORKSPACE.
  */
 int ssm_ssd_fwd(const void* x, const void* delta, const void* z,

@@ -361,7 +361,7 @@ def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: b
     """SSD (Mamba-2 style) layer with a scalar decay per head.
 
     x, z: (batch, L, H, 64); delta: (batch, L, H); B, C: (batch, L, N) with N
-    = 64 or 128, all bfloat16; A, D, dt_bias: (H,) float32; h0: (batch, H,
+    = 64, 128 or 256, all bfloat16; A, D, dt_bias: (H,) float32; h0: (batch, H,
     64, N) float32; workspace: a device tensor of at least
     ssd_workspace_bytes(...) bytes (allocated here when None).  Returns
     (y, h_last).
@@ -386,7 +386,7 @@ def ssd_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, return_last_state: b
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", (batch, L, H, P), dt, dev)
     h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev) if return_last_state else None
-    if io == SSM_BF16 and N in (64, 128) and P == 64:
+    if io == SSM_BF16 and N in (64, 128, 256) and P == 64:
         nws = ssd_workspace_bytes(batch, L, H, N, P)
         if workspace is None:
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)

@@ -72,11 +72,15 @@ __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
 }
 
 // LDS of ssd_chunked: 48 KB for N = 128, so three workgroups fit on a CU
-// and every (batch row, head) of a 640-sequence launch is resident at once.
+// and every (batch row, head) of a 640-sequence launch is resident at once;
+// 79 KB for N = 256 (two per CU).
 template <int N>
 struct alignas(16) Smem {
-    static constexpr int kLdB = N + 24;   // transposing reads conflict-free
-    static constexpr int kLdS = N + 8;    // 16-byte reads and 8-byte writes conflict-free
+    // Row strides, in 4-byte banks modulo 64: B rows 12 (N + 24 = 76 or 140
+    // dwords) keep the transposing reads conflict-free, state-copy rows 4
+    // (N + 8) the 16-byte reads and 8-byte writes.
+    static constexpr int kLdB = N + 24;
+    static constexpr int kLdS = N + 8;
     static constexpr int kLdX = kP + 16;
     uint16_t Bs[kQ][kLdB];      // B rows of the chunk            [i][n]
     uint16_t Xs[kQ][kLdX];      // x rows                         [i][p]
@@ -85,18 +89,18 @@ struct alignas(16) Smem {
     float Dl[kQ];               // Delta_t
     float Wt[kQ];               // exp(S_end - S_t) Delta_t
     // Each wavefront's output rows pass through LDS (fp32, 16 rows of 64
-    // channels, row stride kLdY floats) to be stored row by row.  When a row of
-    // St holds 256 bytes the wavefront's own 16 St rows serve (it rewrites them
-    // only afterwards); otherwise a separate area.
-    static constexpr int kLdY = 68;
+    // channels, row stride kLdY floats, 4 banks modulo 64) to be stored row by
+    // row.  When a row of St holds 256 bytes the wavefront's own 16 St rows
+    // serve, at St's stride (it rewrites them only afterwards); otherwise a
+    // separate area.
     static constexpr bool kYinSt = kLdS * 2 >= kP * 4;
+    static constexpr int kLdY = kYinSt ? kLdS / 2 : kP + 4;
     float Ys[kYinSt ? 0 : 4][16][kLdY];
 };
 
 template <int N>
 __device__ __forceinline__ float* ystage(Smem<N>& sm, int w) {
     if constexpr (Smem<N>::kYinSt) {
-        static_assert(Smem<N>::kLdS * 2 == Smem<N>::kLdY * 4, "St rows and staging rows must have the same stride");
         return reinterpret_cast<float*>(&sm.St[16 * w][0]);
     } else {
         return &sm.Ys[w][0][0];
@@ -281,7 +285,7 @@ __device__ __forceinline__ void publish_state(Smem<N>& sm, const f32x4 (&st)[N /
 }
 
 template <int N, bool GATED>
-__global__ __launch_bounds__(kThreads, 3) void ssd_chunked(SsdArgs a) {
+__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdArgs a) {
     constexpr int NB = N / 16;            // 16-row blocks of the state's n
     constexpr int KS = N / 32;            // k-steps of a product over n
     __shared__ Smem<N> sm;
@@ -478,6 +482,7 @@ hipError_t ssd_launch(const SsdArgs& a, hipStream_t stream) {
     switch (a.N) {
         case 64: return launch_ssd_n<64>(a, stream);
         case 128: return launch_ssd_n<128>(a, stream);
+        case 256: return launch_ssd_n<256>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

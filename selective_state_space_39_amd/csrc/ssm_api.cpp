@@ -455,7 +455,8 @@ int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b,
 static int ssd_check(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype) {
     if (io_dtype != SSM_BF16)
         return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 io (its products run on bf16 matrix cores)");
-    if (N != 64 && N != 128) return fail(SSM_ERR_N, "N = %lld: the SSD layer is built for N = 64 or 128", (long long)N);
+    if (N != 64 && N != 128 && N != 256)
+        return fail(SSM_ERR_N, "N = %lld: the SSD layer is built for N = 64, 128 or 256", (long long)N);
     if (P != 64) return fail(SSM_ERR_SHAPE, "P = %lld: the SSD layer is built for 64 channels per head", (long long)P);
     if (batch < 1 || L < 1 || H < 1)
         return fail(SSM_ERR_SHAPE, "batch, L and H must be >= 1 (got %lld, %lld, %lld)", (long long)batch,

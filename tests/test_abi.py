@@ -310,7 +310,8 @@ def test_ssd_workspace_formula():
     for batch, L in ((1, 1), (2, 64), (2, 65), (8, 2048), (3, 1000)):
         assert f(batch, L, 80, 64, 128, 1) == batch * -(-L // 64) * 64 * 64 * 2
         assert f(batch, L, 80, 64, 64, 1) == batch * -(-L // 64) * 64 * 64 * 2
-    assert f(1, 100, 4, 64, 96, 1) == E_N
+        assert f(batch, L, 80, 64, 256, 1) == batch * -(-L // 64) * 64 * 64 * 2
+    assert f(1, 100, 4, 64, 96, 1) == E_N and f(1, 100, 4, 64, 512, 1) == E_N
     assert f(1, 100, 4, 32, 128, 1) == E_SHAPE
     assert f(1, 100, 4, 64, 128, 0) == E_DTYPE
     assert f(1, 20_000_000, 1, 64, 64, 1) == E_SHAPE  # a batch row's blocks beyond 32-bit offsets

@@ -15,6 +15,8 @@ pytestmark = pytest.mark.gpu
     (1, 1, 1, 128, True, False),       # one token
     (2, 1000, 4, 128, True, True),     # 16 chunks, ragged
     (3, 130, 5, 64, True, True),       # N = 64, ragged
+    (2, 300, 3, 256, True, True),      # N = 256, ragged
+    (1, 64, 2, 256, False, False),     # N = 256, one chunk
 ])
 def test_ssd_matches_oracle(batch, L, H, N, gated, h0):
     s = inputs.make_ssd_inputs(batch, L, H, N=N, seed=(39, 6000 + L + H), gated=gated, with_h0=h0)
