@@ -280,7 +280,7 @@ def bench_decode(args):
                         "avg_launch_ms": round(avg_ms, 5),
                         "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters"
                                 + (", + the conv state read and written" if conv else "") + ")"},
-           "mall_flushed": flushed_timing(step, stream, abytes, batch * D)}
+           "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, batch * D)}
     print(json.dumps(out), flush=True)
 
 
@@ -365,7 +365,7 @@ def bench_bwd(args, k):
                         "work": f"{BWD_SLOTS_PER_ELEMENT} fp32 VALU slots (= {2 * BWD_SLOTS_PER_ELEMENT} "
                                 f"FMA-equivalent flops) per element x {E} elements per launch"},
            "kernels": kernels,
-           "mall_flushed": flushed_timing(step, stream, abytes, E)}
+           "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
     print(json.dumps(out), flush=True)
 
 
@@ -443,7 +443,7 @@ def bench_ssd(args):
            "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": PEAK_BF16_TFLOPS,
                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops},
            "kernels": breakdown,
-           "mall_flushed": flushed_timing(step, stream, abytes, E)}
+           "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
     print(json.dumps(out), flush=True)
 
 
@@ -455,6 +455,8 @@ def main():
     ap.add_argument("--workload", default="mamba-130m-layer", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flushed", action="store_true",
+                    help="skip the cache-flushed single steps (kernel traces then cover the timed loops only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (profile it for counter calibration)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -579,7 +581,7 @@ def main():
            "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
                    "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes},
            "roofline": roofline, "kernels": kernels,
-           "mall_flushed": flushed_timing(step, stream, abytes, E)}
+           "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
     if not args.no_cpu_baseline and not conv:
         out["cpu_baseline"] = cpu_baseline(s)
     print(json.dumps(out), flush=True)
