@@ -109,7 +109,10 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dty
  *   y               required output, (batch, L, D) io dtype.
  *   h_last          NULL = not wanted, else (batch, D, N) float32 output.
  *   chunk_len       0 = the library's plan for the MI355X; else a positive
- *                   multiple of 32 (a smaller, ragged last chunk is allowed).
+ *                   multiple of 32 (a smaller, ragged last chunk is allowed)
+ *                   of at most (2^31 - 1) / (4 D) tokens, so that a chunk's
+ *                   rows stay within 32-bit byte offsets (SSM_ERR_SHAPE
+ *                   otherwise; the library's plan respects the same cap).
  *   workspace       at least ssm_scan_fwd_workspace_bytes(...) bytes, 16-byte
  *                   aligned; may be NULL when that size is 0.
  * Alignment: io tensors to their element size; B and C to 16 bytes; float32
@@ -237,7 +240,8 @@ int ssm_scan_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dty
  *   dh0             (batch, D, N) float32 output or NULL (not wanted); the
  *                   gradient with respect to the starting state, also when
  *                   h0 is NULL.
- *   chunk_len       0 = the library's plan; else a positive multiple of 32.
+ *   chunk_len       0 = the library's plan; else a positive multiple of 32,
+ *                   capped as for ssm_scan_fwd.
  *   workspace       at least ssm_scan_bwd_workspace_bytes(...) bytes,
  *                   256-byte aligned, required.
  * Alignment as for ssm_scan_fwd (dout, dx, ddelta, dz like x).  No output may

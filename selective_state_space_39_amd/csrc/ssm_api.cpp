@@ -120,12 +120,29 @@ double est_plan(int64_t batch, int64_t D, int64_t L, int64_t len) {
     return t;
 }
 
-int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
+// The kernels address a chunk's rows of x, delta, z and y (and their
+// gradients) with 32-bit byte offsets from the chunk's first row: a chunk may
+// hold at most 2 GiB at 4 bytes per element.
+int64_t max_chunk_len(int64_t D) { return ((int64_t(1) << 31) - 1) / (D * 4) / kChunkAlign * kChunkAlign; }
+
+int check_chunk_len(int64_t D, int64_t chunk_len) {
     if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
         return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
                     (long long)chunk_len, (long long)kChunkAlign);
+    const int64_t cap = max_chunk_len(D);
+    if (cap < kChunkAlign)
+        return fail(SSM_ERR_SHAPE, "D = %lld: even a %lld-token chunk exceeds 2 GiB", (long long)D,
+                    (long long)kChunkAlign);
+    if (chunk_len > cap)
+        return fail(SSM_ERR_SHAPE, "chunk_len = %lld: a chunk of %lld channels would exceed 2 GiB (at most %lld tokens)",
+                    (long long)chunk_len, (long long)D, (long long)cap);
+    return SSM_OK;
+}
+
+int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
+    if (int rc = check_chunk_len(D, chunk_len)) return rc;
     if (chunk_len == 0) {
-        const int64_t whole = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        const int64_t whole = std::min((L + kChunkAlign - 1) / kChunkAlign * kChunkAlign, max_chunk_len(D));
         int64_t best = whole;
         double best_t = est_plan(batch, D, L, whole);
         for (int64_t len = whole - kChunkAlign; len >= kMinChunk; len -= kChunkAlign) {
@@ -176,11 +193,9 @@ double est_bwd(int64_t batch, int64_t D, int64_t L, int64_t len) {
 }
 
 int make_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, BwdPlan& p) {
-    if (chunk_len < 0 || (chunk_len > 0 && chunk_len % kChunkAlign != 0))
-        return fail(SSM_ERR_SHAPE, "chunk_len = %lld must be 0 or a positive multiple of %lld",
-                    (long long)chunk_len, (long long)kChunkAlign);
+    if (int rc = check_chunk_len(D, chunk_len)) return rc;
     if (chunk_len == 0) {
-        const int64_t whole = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        const int64_t whole = std::min((L + kChunkAlign - 1) / kChunkAlign * kChunkAlign, max_chunk_len(D));
         int64_t best = whole;
         double best_t = est_bwd(batch, D, L, whole);
         for (int64_t len = whole - kChunkAlign; len >= kChunkAlign; len -= kChunkAlign) {

@@ -54,6 +54,21 @@ def test_plan_and_workspace():
         assert cl % 32 == 0 and nc == -(-l // cl) and nc >= 1
 
 
+def test_chunk_bytes_limit():
+    """A chunk's rows are addressed with 32-bit offsets: at most 2 GiB per chunk (4 bytes per element)."""
+    L = binding.lib()
+    # explicit chunk: 4096 tokens x 2^22 channels x 4 B = 64 GiB -> rejected, forward and backward
+    assert L.ssm_scan_fwd_workspace_bytes(1, 4096, 1 << 22, 16, 1, 4096) == E_SHAPE
+    assert L.ssm_scan_bwd_workspace_bytes(1, 4096, 1 << 22, 16, 1, 4096) == E_SHAPE
+    # automatic plan: capped at (2^31 - 1) / (2^22 * 4) rounded down to 32 = 96 tokens
+    cl, nc = binding.plan(1, 1024, 1 << 22, 1, 0)
+    assert cl <= 96 and cl % 32 == 0 and nc == -(-1024 // cl)
+    cl, nc = binding.bwd_plan(1, 1024, 1 << 22, 1, 0)
+    assert cl <= 96 and cl % 32 == 0
+    # not even 32 tokens fit
+    assert L.ssm_scan_fwd_workspace_bytes(1, 64, 1 << 26, 16, 1, 0) == E_SHAPE
+
+
 @pytest.mark.parametrize("args,code", [
     ((1, 10, 8, 8, 1, 0), E_N),
     ((1, 10, 8, 16, 7, 0), E_DTYPE),
