@@ -184,8 +184,11 @@ __device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t bid) {
     const float* S = a.S + b * ncar * a.D + d;
     float* H = a.H + (b * ncar * kN + n) * a.D + d;
     const int64_t hs = kN * a.D;                                // H stride between carries
-    for (int64_t k0 = 0; k0 < ncar; k0 += kScanBlk) {
-        float Sv[kScanBlk], Hv[kScanBlk];
+    // Blocks of kScanBlk carries, double-buffered: the next block's loads are
+    // issued before this block's prefix stores (written in that order, so the
+    // compiler, which cannot prove they touch other addresses, keeps it), and
+    // a block costs one memory round trip only at the start.
+    auto load_blk = [&](int64_t k0, float (&Sv)[kScanBlk], float (&Hv)[kScanBlk]) {
 #pragma unroll
         for (int k = 0; k < kScanBlk; ++k) {
             const int64_t kk = k0 + k < ncar ? k0 + k : ncar - 1;
@@ -193,6 +196,8 @@ __device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t bid) {
             Sv[k] = S[c * a.D];
             Hv[k] = H[c * hs];
         }
+    };
+    auto fold_blk = [&](int64_t k0, const float (&Sv)[kScanBlk], const float (&Hv)[kScanBlk]) {
 #pragma unroll
         for (int k = 0; k < kScanBlk; ++k) {
             if (k0 + k < ncar) {                                  // wave-uniform
@@ -201,6 +206,15 @@ __device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t bid) {
                 H[c * hs] = h;
             }
         }
+    };
+    float S0[kScanBlk], H0[kScanBlk], S1[kScanBlk], H1[kScanBlk];
+    load_blk(0, S0, H0);
+    for (int64_t k0 = 0; k0 < ncar; k0 += 2 * kScanBlk) {
+        if (k0 + kScanBlk < ncar) load_blk(k0 + kScanBlk, S1, H1);
+        fold_blk(k0, S0, H0);
+        if (k0 + kScanBlk >= ncar) break;
+        if (k0 + 2 * kScanBlk < ncar) load_blk(k0 + 2 * kScanBlk, S0, H0);
+        fold_blk(k0 + kScanBlk, S1, H1);
     }
 }
 
