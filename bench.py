@@ -201,6 +201,20 @@ def cpu_baseline(s, min_seconds=10.0, max_passes=12):
                       f"NumPy float64 elementwise loop, single-threaded (BLAS pool {blas_threads} unused)"}
 
 
+def cpu_sampled(call, elements_per_call, what, min_seconds=10.0, max_calls=400):
+    """The float64 oracle as it stands, on the host: call(i) runs the i-th piece
+    of the workload (a strip of channels or heads, or one decode step) and is
+    repeated until min_seconds have passed; the rate is elements per second."""
+    calls, elapsed = 0, 0.0
+    while calls < max_calls and (calls == 0 or elapsed < min_seconds):
+        t0 = time.perf_counter()
+        call(calls)
+        elapsed += time.perf_counter() - t0
+        calls += 1
+    return {"value": calls * elements_per_call / elapsed, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} x {what}, {elapsed:.1f} s; NumPy float64, single-threaded"}
+
+
 def decode_bytes(batch, D, N=16, io_bytes=2):
     """State read and written; x, delta, z read and y written; B, C read; A, Dskip, dt_bias read."""
     return batch * D * (2 * N * 4 + 4 * io_bytes) + 2 * batch * N * io_bytes + D * (N + 2) * 4
@@ -281,6 +295,18 @@ def bench_decode(args):
                         "work": f"{abytes} algorithmic bytes per launch (136 B per (b, d) + B/C + parameters"
                                 + (", + the conv state read and written" if conv else "") + ")"},
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, batch * D)}
+    if not args.no_cpu_baseline:
+        import oracle
+        st = {"h": h0.astype("float64"), "conv": cp.init if conv else None}
+
+        def one(i):
+            t = toks[i & 7]
+            if conv:
+                _, st["h"], st["conv"] = oracle.conv_state_update(st["conv"], st["h"], t.x, cp.w, cp.b, t.delta, A,
+                                                                  t.B, t.C, Dskip, dt_bias, z=t.z, io="bf16")
+            else:
+                _, st["h"] = oracle.state_update(st["h"], t.x, t.delta, A, t.B, t.C, Dskip, dt_bias, z=t.z, io="bf16")
+        out["cpu_baseline"] = cpu_sampled(one, batch * D, f"chained decode steps of the whole {batch}x{D} state")
     print(json.dumps(out), flush=True)
 
 
@@ -366,6 +392,16 @@ def bench_bwd(args, k):
                                 f"FMA-equivalent flops) per element x {E} elements per launch"},
            "kernels": kernels,
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
+    if not args.no_cpu_baseline:
+        import oracle
+        cs = 128
+
+        def one(i):
+            g = slice(cs * i % D, cs * i % D + cs)
+            oracle.scan_bwd(s.x[..., g], s.delta[..., g], s.A[g], s.B, s.C, s.Dskip[g], s.dt_bias[g], go.dout[..., g],
+                            z=s.z[..., g], io=io)
+        out["cpu_baseline"] = cpu_sampled(one, batch * L * cs,
+                                          f"{cs}-channel strips of the workload ({batch}x{L}x{cs}, all tokens)")
     print(json.dumps(out), flush=True)
 
 
@@ -444,6 +480,16 @@ def bench_ssd(args):
                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops},
            "kernels": breakdown,
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = 4
+
+        def one(i):
+            g = slice(hs * i % H, hs * i % H + hs)
+            oracle.ssd_fwd(s.x[:, :, g], s.delta[:, :, g], s.A[g], s.B, s.C, s.Dskip[g], s.dt_bias[g], z=s.z[:, :, g],
+                           io=s.io)
+        out["cpu_baseline"] = cpu_sampled(one, batch * L * hs * P,
+                                          f"{hs}-head strips of the workload ({batch}x{L}x{hs}x{P}, all tokens)")
     print(json.dumps(out), flush=True)
 
 
@@ -584,6 +630,11 @@ def main():
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
     if not args.no_cpu_baseline and not conv:
         out["cpu_baseline"] = cpu_baseline(s)
+    elif not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_sampled(
+            lambda i: oracle.conv_scan_fwd(s.x, cp.w, cp.b, s.delta, s.A, s.B, s.C, s.Dskip, s.dt_bias, z=s.z, io=io),
+            E, f"full passes of the workload ({batch}x{L}x{D}, convolution included)")
     print(json.dumps(out), flush=True)
 
 
