@@ -497,7 +497,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks take tens of milliseconds of load to settle: 300 untimed
+    # steps (50 ms for the 130M-layer scan) put the timed steps in steady state;
+    # after 5 the step time still reads ~10 % high.
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mamba-130m-layer", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

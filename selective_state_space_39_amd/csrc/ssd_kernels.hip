@@ -244,6 +244,24 @@ __device__ __forceinline__ void load_z(const SeqIO& io, int t0, int w, OwnRegs<N
     for (int k = 0; k < 2; ++k) o.z[k] = ld16(io.z, v, static_cast<uint32_t>(t0 + 8 * k) * io.xrow);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: four row
+// shifts scan each row of 16 lanes, then row_bcast:15 and row_bcast:31 carry
+// the row totals forward (the gfx9-family broadcasts).  Lanes a shift or
+// broadcast does not reach add 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_src(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float s) {
+    s += dpp_src<0x111, 0xf>(s);        // row_shr:1
+    s += dpp_src<0x112, 0xf>(s);        // row_shr:2
+    s += dpp_src<0x114, 0xf>(s);        // row_shr:4
+    s += dpp_src<0x118, 0xf>(s);        // row_shr:8
+    s += dpp_src<0x142, 0xa>(s);        // row_bcast:15 into rows 1 and 3
+    s += dpp_src<0x143, 0xc>(s);        // row_bcast:31 into rows 2 and 3
+    return s;
+}
+
 // Stage one chunk: x and B rows into LDS; wavefront 0 scans the step sizes
 // (lane = token) and publishes S, Delta and the state-update weights.
 template <int N>
@@ -251,13 +269,8 @@ __device__ __forceinline__ void stage_chunk(Smem<N>& sm, const StageRegs<N>& r, 
     const int tid = threadIdx.x, l = tid & 63;
     if (w == 0) {
         const float dt = l < nt ? s6::softplus(from_bf16(r.dl) + bias) : 0.0f;
-        float s = dt * A * kLog2e;
-#pragma unroll
-        for (int off = 1; off < kQ; off <<= 1) {               // inclusive scan over the wavefront
-            const float o = __shfl_up(s, off);
-            if (l >= off) s += o;
-        }
-        const float s_end = __shfl(s, kQ - 1);
+        const float s = wave_inclusive_sum(dt * A * kLog2e);
+        const float s_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), kQ - 1));
         sm.S2[l] = s;
         sm.Dl[l] = dt;
         sm.Wt[l] = __builtin_amdgcn_exp2f(s_end - s) * dt;
@@ -370,8 +383,8 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
                                      lo_bf16(gw.z), hi_bf16(gw.z), lo_bf16(gw.w), hi_bf16(gw.w)};
                 float m[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    m[j] = i0 + j <= tw ? gi[j] * (__builtin_amdgcn_exp2f(s2t - si[j]) * di[j]) : 0.0f;
+                for (int j = 0; j < 8; ++j)     // above the diagonal: exp2(-inf) = +0, no branch
+                    m[j] = gi[j] * (__builtin_amdgcn_exp2f(i0 + j <= tw ? s2t - si[j] : -__builtin_inff()) * di[j]);
                 mop[ks] = pack8(m);
             }
         }
