@@ -44,9 +44,12 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12        # 78.64, fp32 vector without packed math
 SLOTS_PER_ELEMENT = 112
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
-WORKLOADS = {"mamba-130m-layer": 2, "mamba-2.8b-layer": 3, "long-context-128k": 4, "decode-256x5120": 5,
-             "mamba-130m-layer-bwd": 2, "mamba-2.8b-layer-bwd": 3,
-             "mamba-130m-layer-conv": 2, "decode-256x5120-conv": 5, "mamba2-2.7b-layer": 6}
+# bench workload -> (what is timed, the named input workload it runs on)
+WORKLOADS = {"mamba-130m-layer": ("scan", "mamba-130m-layer"), "mamba-2.8b-layer": ("scan", "mamba-2.8b-layer"),
+             "long-context-128k": ("scan", "long-context-128k"), "decode-256x5120": ("decode", None),
+             "mamba-130m-layer-bwd": ("bwd", "mamba-130m-layer"), "mamba-2.8b-layer-bwd": ("bwd", "mamba-2.8b-layer"),
+             "mamba-130m-layer-conv": ("conv", "mamba-130m-layer"), "decode-256x5120-conv": ("decode", None),
+             "mamba2-2.7b-layer": ("ssd", None)}
 PEAK_BF16_TFLOPS = 2500.0           # dense bf16 matrix-core peak
 CONV_K = 4                          # width of the fused local convolution in the -conv workloads
 CONV_SLOTS = 10                     # per element: 4 FMA + silu (exp 2, rcp 2, add, mul)
@@ -244,7 +247,7 @@ def bench_decode(args):
 
     conv = args.workload.endswith("-conv")
     if conv:
-        cp = inputs.make_conv_params(batch, D, CONV_K, io="bf16", seed=(39, 5), with_init=True)
+        cp = inputs.make_conv_params(batch, D, CONV_K, io="bf16", seed=inputs.DECODE_WORKLOAD["seed"], with_init=True)
         cw, cb = f32(cp.w), f32(cp.b)
         cstate = bf(cp.init)
 
@@ -316,14 +319,15 @@ def bwd_algorithmic_bytes(batch, L, D, N=16, io_bytes=2):
     return (7 * batch * L * D * io_bytes + 2 * batch * L * N * (io_bytes + 4) + 2 * D * (N + 2) * 4)
 
 
-def bench_bwd(args, k):
+def bench_bwd(args, name):
     """ssm_scan_bwd on a whole-sequence workload: gradients with respect to every input."""
     import torch
     from selective_state_space_39_amd import binding, inputs
-    s = inputs.make_config(k)
+    s = inputs.make_workload(name)
     batch, L, D, N = s.shape
     io = s.io
-    go = inputs.make_grad_outputs(batch, L, D, N, io=io, seed=(39, k), with_dh_last=False)
+    go = inputs.make_grad_outputs(batch, L, D, N, io=io, seed=inputs.SCAN_WORKLOADS[name]["seed"],
+                                  with_dh_last=False)
     dev = torch.device("cuda:0")
 
     def to_dev(a):
@@ -423,7 +427,7 @@ def bench_ssd(args):
     import torch
     from selective_state_space_39_amd import binding, inputs
     w = inputs.SSD_WORKLOAD
-    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=(39, 6))
+    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=w["seed"])
     batch, L, H, P, N = s.shape
     dev = torch.device("cuda:0")
     bf = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
@@ -529,14 +533,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    k = WORKLOADS[args.workload]
-    if k == 6:
+    kind, name = WORKLOADS[args.workload]
+    if kind == "ssd":
         return bench_ssd(args)
-    if k == 5:
+    if kind == "decode":
         return bench_decode(args)
-    if args.workload.endswith("-bwd"):
-        return bench_bwd(args, k)
-    s = inputs.make_config(k)
+    if kind == "bwd":
+        return bench_bwd(args, name)
+    s = inputs.make_workload(name)
     batch, L, D, N = s.shape
     io = s.io
     dev = torch.device("cuda:0")
@@ -557,7 +561,7 @@ def main():
 
     conv = args.workload.endswith("-conv")
     if conv:
-        cp = inputs.make_conv_params(batch, D, CONV_K, io=io, seed=(39, k))
+        cp = inputs.make_conv_params(batch, D, CONV_K, io=io, seed=inputs.SCAN_WORKLOADS[name]["seed"])
         cw, cb = f32(cp.w), f32(cp.b)
 
         def step():

@@ -33,15 +33,21 @@ import numpy as np
 N_STATE = 16
 SEED_ROOT = 39
 
-# Named workloads. Sizes follow the S6 layer shapes they are named after; the
-# "D" here is the already-expanded inner width (two times the model width).
-CONFIGS = {
-    1: dict(name="tiny-f32", batch=1, L=256, D=16, io="f32", delta="normal", delta_sigma=0.5),
-    2: dict(name="mamba-130m-layer", batch=8, L=2048, D=1536, io="bf16", delta="normal", delta_sigma=0.5),
-    3: dict(name="mamba-2.8b-layer", batch=4, L=2048, D=5120, io="bf16", delta="normal", delta_sigma=1.0),
-    4: dict(name="long-context-128k", batch=1, L=131072, D=2048, io="bf16", delta="blocks", block=64),
-    5: dict(name="decode-256x5120", batch=256, D=5120, io="bf16", delta="normal", delta_sigma=0.5, steps=1000),
+# Named whole-sequence workloads and the seed each is drawn from. Sizes follow
+# the S6 layer shapes they are named after; the "D" here is the already-expanded
+# inner width (two times the model width).
+SCAN_WORKLOADS = {
+    "tiny-f32": dict(batch=1, L=256, D=16, io="f32", delta="normal", delta_sigma=0.5, seed=(SEED_ROOT, 1)),
+    "mamba-130m-layer": dict(batch=8, L=2048, D=1536, io="bf16", delta="normal", delta_sigma=0.5,
+                             seed=(SEED_ROOT, 2)),
+    "mamba-2.8b-layer": dict(batch=4, L=2048, D=5120, io="bf16", delta="normal", delta_sigma=1.0,
+                             seed=(SEED_ROOT, 3)),
+    "long-context-128k": dict(batch=1, L=131072, D=2048, io="bf16", delta="blocks", block=64,
+                              seed=(SEED_ROOT, 4)),
 }
+# Chained single-token decode against a cached state: (batch, D), 1000 steps,
+# drawn from decode_params / decode_token.
+DECODE_WORKLOAD = dict(name="decode-256x5120", batch=256, D=5120, io="bf16", steps=1000, seed=(SEED_ROOT, 5))
 
 
 # ----------------------------------------------------------------------------
@@ -266,7 +272,7 @@ class SsdInputs:
         return b, L, H, P, self.B.shape[-1]
 
 
-SSD_WORKLOAD = dict(name="mamba2-2.7b-layer", batch=8, L=2048, H=80, P=64, N=128, io="bf16")
+SSD_WORKLOAD = dict(name="mamba2-2.7b-layer", batch=8, L=2048, H=80, P=64, N=128, io="bf16", seed=(SEED_ROOT, 6))
 
 
 def make_ssd_inputs(batch: int, L: int, H: int, P: int = 64, N: int = 128, io: str = "bf16",
@@ -293,12 +299,10 @@ def make_ssd_inputs(batch: int, L: int, H: int, P: int = 64, N: int = 128, io: s
                      h0=h0)
 
 
-def make_config(k: int) -> ScanInputs:
-    """The whole-sequence workload number k (1..4), seeded with (39, k)."""
-    c = CONFIGS[k]
-    if k == 5:
-        raise ValueError("config 5 is a decode workload: use decode_params / decode_token")
-    return make_scan_inputs(c["batch"], c["L"], c["D"], N_STATE, c["io"], seed=(SEED_ROOT, k),
+def make_workload(name: str) -> ScanInputs:
+    """The named whole-sequence workload (SCAN_WORKLOADS), seeded as listed there."""
+    c = SCAN_WORKLOADS[name]
+    return make_scan_inputs(c["batch"], c["L"], c["D"], N_STATE, c["io"], seed=c["seed"],
                             delta=c["delta"], delta_sigma=c.get("delta_sigma", 0.5),
                             block=c.get("block", 64))
 

@@ -66,8 +66,9 @@ def test_bwd_without_dh0():
 
 def test_bwd_full_size_mamba130m_layer():
     """The 130M-layer workload (8 x 2048 x 1536, bf16, S4D-real A) at the automatic plan."""
-    s = inputs.make_config(2)
-    go = inputs.make_grad_outputs(8, 2048, 1536, io="bf16", seed=(39, 2), with_dh_last=False)
+    s = inputs.make_workload("mamba-130m-layer")
+    go = inputs.make_grad_outputs(8, 2048, 1536, io="bf16", seed=inputs.SCAN_WORKLOADS["mamba-130m-layer"]["seed"],
+                                  with_dh_last=False)
     log(f"full-size bwd plan {binding.bwd_plan(8, 2048, 1536, 1, 0)}")
     g = gpu_bwd(s, go, h0=False)
     log("oracle (channel strips) ...")

@@ -59,8 +59,9 @@ def test_conv_scan_stream_split():
 
 def test_conv_scan_full_size_sampled():
     """The 130M-layer shape with a width-4 convolution, at the automatic plan, on 64 sampled channels."""
-    s = inputs.make_config(2)
-    cp = inputs.make_conv_params(8, 1536, 4, io="bf16", seed=(39, 2), with_init=False)
+    s = inputs.make_workload("mamba-130m-layer")
+    cp = inputs.make_conv_params(8, 1536, 4, io="bf16", seed=inputs.SCAN_WORKLOADS["mamba-130m-layer"]["seed"],
+                                 with_init=False)
     y, h, _ = gpu_conv_scan(s, cp, conv_last=False)
     ch = np.random.default_rng([39, 5200]).choice(1536, size=64, replace=False)
     ry, rh = oracle_conv_scan(s, cp, channels=ch)

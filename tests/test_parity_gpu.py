@@ -29,9 +29,10 @@ def _check_scan(s, chunk_len=0, gated=True, h0=None, channels=None, what=""):
     return ey, eh
 
 
-def test_config1_tiny_f32():
-    s = inputs.make_config(1)
-    _check_scan(s, what="config1")
+def test_tiny_f32():
+    """1 x 256 x 16, every tensor float32."""
+    s = inputs.make_workload("tiny-f32")
+    _check_scan(s, what="tiny-f32")
 
 
 @pytest.mark.parametrize("batch,L,D,chunk,gated,h0,io", [
@@ -48,26 +49,28 @@ def test_small_cases(batch, L, D, chunk, gated, h0, io):
     _check_scan(s, chunk_len=chunk, gated=gated, h0=s.h0, what=f"small {batch}x{L}x{D}")
 
 
-def test_config2_full():
-    s = inputs.make_config(2)
-    _check_scan(s, what="config2")
+def test_mamba130m_layer_full():
+    """8 x 2048 x 1536, bf16, every output."""
+    s = inputs.make_workload("mamba-130m-layer")
+    _check_scan(s, what="mamba-130m-layer")
 
 
-def test_config3_full():
-    s = inputs.make_config(3)
-    _check_scan(s, what="config3")
+def test_mamba28b_layer_full():
+    """4 x 2048 x 5120, bf16, every output."""
+    s = inputs.make_workload("mamba-2.8b-layer")
+    _check_scan(s, what="mamba-2.8b-layer")
 
 
-def test_config4_sampled_channels():
+def test_long_context_128k_sampled_channels():
     """Long context: every token of 64 sampled channels (spread over the chunk
     groups, first and last channel included) against the oracle."""
-    s = inputs.make_config(4)
+    s = inputs.make_workload("long-context-128k")
     r = np.random.default_rng(4)
     ch = np.unique(np.concatenate([[0, 1, 63, 64, 1023, 1024, 2046, 2047], r.choice(2048, 56, replace=False)]))
-    _check_scan(s, channels=ch, what="config4")
+    _check_scan(s, channels=ch, what="long-context-128k")
 
 
-def test_config5_decode_chain():
+def test_decode_256x5120_chain():
     """1000 chained decode steps: y and the state of a 16 x 256 sample of
     (batch row, channel) pairs against the oracle's own float64 chain, which
     starts from the same float32 state and is never re-seeded from the GPU."""
