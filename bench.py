@@ -17,13 +17,17 @@ average.  A third pass brackets every kernel for the per-kernel breakdown.
 
 Roofline.  On MI355X this path is bound by vector-ALU issue, not HBM: every
 element needs 16 exponentials and ~64 fp32 multiply/FMA operations for 8 bytes
-of HBM traffic.  The work unit is an fp32 VALU issue slot of one lane (a
-full-rate instruction; transcendentals issue at half rate and count as two),
-reported as FMA-equivalent flops (2 per slot) against the chip's fp32 vector
-peak without packed math: 256 CUs x 64 lanes x 2 x 2.4 GHz = 78.64 TFLOP/s.
-The algorithmic work per (b, t, d) element is 112 slots = 224 flops:
-  16 states x (mul for Delta*A, exp = 2, mul for Delta*x*B, fma for h, fma for y) = 96
-  softplus (exp 2 + log 2 + 3) = 7, Delta*x 1, skip 1, silu gate (exp 2 + rcp 2 + 3) = 7.
+of HBM traffic.  The work unit is an fp32 VALU issue slot of one lane at the
+full rate: gfx950 issues a wave64 fp32 add/mul/FMA whose operands are all
+VGPRs every 2 cycles per SIMD (32 lanes per cycle; measured), which is the
+published fp32 vector peak without packed math: 256 CUs x 4 SIMDs x 32 lanes
+x 2 flops x 2.4 GHz = 157.3 TFLOP/s.  Transcendentals (exp, log, rcp) run at
+a quarter of that rate and count as four slots (an operand read from an SGPR
+halves an instruction's rate; that is the kernel's cost, not the method's).
+Reported as FMA-equivalent flops (2 per slot).  The algorithmic work per
+(b, t, d) element is 152 slots = 304 flops:
+  16 states x (mul for Delta*A, exp = 4, mul for Delta*x*B, fma for h, fma for y) = 128
+  softplus (exp 4 + log 4 + 3) = 11, Delta*x 1, skip 1, silu gate (exp 4 + rcp 4 + 3) = 11.
 The achieved HBM rate (algorithmic bytes / step time) and its fraction of
 8 TB/s are reported next to it.
 """
@@ -41,8 +45,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan elements/s (B·L·D) and achieved HBM GB/s vs peak, 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
-PEAK_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12        # 78.64, fp32 vector without packed math
-SLOTS_PER_ELEMENT = 112
+PEAK_VALU_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12    # 157.3, fp32 vector (VGPR operands, no packed math)
+SLOTS_PER_ELEMENT = 152
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
 # bench workload -> (what is timed, the named input workload it runs on)
 WORKLOADS = {"mamba-130m-layer": ("scan", "mamba-130m-layer"), "mamba-2.8b-layer": ("scan", "mamba-2.8b-layer"),
@@ -52,15 +56,16 @@ WORKLOADS = {"mamba-130m-layer": ("scan", "mamba-130m-layer"), "mamba-2.8b-layer
              "mamba2-2.7b-layer": ("ssd", None)}
 PEAK_BF16_TFLOPS = 2500.0           # dense bf16 matrix-core peak
 CONV_K = 4                          # width of the fused local convolution in the -conv workloads
-CONV_SLOTS = 10                     # per element: 4 FMA + silu (exp 2, rcp 2, add, mul)
-# Backward: algorithmic fp32 VALU issue slots per element (b, t, d), exp/log/rcp counted as 2:
-#   state recompute: softplus 7 + Delta*x 1 + 16 x (mul, exp, mul, fma) 80           = 88
+CONV_SLOTS = 14                     # per element: 4 FMA + silu (exp 4, rcp 4, add, mul)
+# Backward: algorithmic full-rate fp32 VALU slots per element (b, t, d), exp/log/rcp counted as 4:
+#   state recompute: softplus 11 + Delta*x 1 + 16 x (mul, exp, mul, fma) 112          = 124
 #   readout for the gate gradient: 16 FMA + skip                                       = 17
-#   gate gradient (sigmoid, silu, derivative)                                          =  9
-#   adjoint step: 16 x (mu, du, dC term, mul, exp, q, w, sum w A, dA, dB term)          = 176
-#   per-token tail: sigmoid(v) from the softplus exponential, dx, dDelta, ddelta, dD, dbias = 10
+#   gate gradient (sigmoid: exp 4 + rcp 4, silu, derivative: 5)                        = 13
+#   adjoint step: 16 x (mu, du, dC term, mul, exp, q, w, sum w A, dA, dB term)          = 208
+#   per-token tail: sigmoid(v) from the softplus exponential (rcp 4), dx, dDelta,
+#   ddelta, dD, dbias (8)                                                              = 12
 #   channel sums of dB and dC: one add per value per channel                           = 32
-BWD_SLOTS_PER_ELEMENT = 332
+BWD_SLOTS_PER_ELEMENT = 406
 BWD_DOMINANT = "s6_chunk_bwd"
 KERNEL_SOURCES = ["selective_state_space_39_amd/csrc/s6_kernels.hip",
                   "selective_state_space_39_amd/csrc/s6_device.h",
@@ -392,7 +397,7 @@ def bench_bwd(args, name):
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_VALU_TFLOPS, 4),
                         "traffic": measured_traffic(args.workload, BWD_DOMINANT), "kernel": BWD_DOMINANT,
                         "avg_launch_ms": round(avg_ms, 5),
-                        "work": f"{BWD_SLOTS_PER_ELEMENT} fp32 VALU slots (= {2 * BWD_SLOTS_PER_ELEMENT} "
+                        "work": f"{BWD_SLOTS_PER_ELEMENT} full-rate fp32 VALU slots (= {2 * BWD_SLOTS_PER_ELEMENT} "
                                 f"FMA-equivalent flops) per element x {E} elements per launch"},
            "kernels": kernels,
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
@@ -618,7 +623,7 @@ def main():
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_VALU_TFLOPS, 2),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_VALU_TFLOPS, 4), "traffic": traffic,
                 "kernel": dominant, "avg_launch_ms": round(avg_ms, 5),
-                "work": f"{slots} fp32 VALU slots (= {2 * slots} FMA-equivalent flops) "
+                "work": f"{slots} full-rate fp32 VALU slots (= {2 * slots} FMA-equivalent flops) "
                         f"per element x {E} elements per launch" + (" (incl. the width-4 convolution)" if conv else "")}
     kernels = {n: {"launches": c, "avg_ms": round(t / c, 5)} for n, (c, t) in breakdown.items()}
     kernels["_note"] = (f"every kernel bracketed by events in a separate pass: {ms_all:.4f} ms per step "

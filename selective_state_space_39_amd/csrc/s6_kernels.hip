@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_out(S6ScanArgs a) {
 // ---------------------------------------------------------------------------
 // Four lanes per channel, four states per lane: the state rows (64 bytes per
 // channel) are read and written as whole 16-byte vectors by consecutive lanes.
-constexpr int kStepRows = 8;      // batch rows per workgroup (A is loaded once for them)
+// Batch rows per workgroup (A is loaded once for them).  Two beat eight on the
+// 256 x 5120 step (27.1 vs 28.2 us hot, 37.7 vs 42.4 us from HBM): many small
+// workgroups keep more of the state in flight than long per-wavefront runs.
+constexpr int kStepRows = 2;
 
 // Four consecutive io elements (a lane's four B or C entries), loaded as one
 // vector when the tensor is aligned for it (VEC), else element by element, and

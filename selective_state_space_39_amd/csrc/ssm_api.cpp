@@ -91,22 +91,27 @@ int check_shape(int64_t batch, int64_t L, int64_t D, int64_t N, int io) {
 }
 
 // Cost model of the MI355X (1024 SIMDs) used by the automatic plan, fitted to
-// measured kernel times (us, bf16 io, N = 16).  A pass with W wavefronts puts
-// w = ceil(W / 1024) on each SIMD, and its makespan is w x (tokens per chunk)
-// x (time per wavefront-token at w waves per SIMD): a lone wave cannot hide
-// its own latencies, and from about four waves per SIMD the VALU stays busy.
-// The carry scan costs ~4 us plus a per-carry term set by its traffic (or by
-// its latency when there are few channels); every extra launch ~4 us.
+// measured kernel times (us, bf16 io, N = 16, steady clocks).  A pass with W
+// wavefronts puts w = ceil(W / 1024) on each SIMD, and its makespan is w x
+// (tokens per chunk) x (time per wavefront-token at w waves per SIMD): a lone
+// wave cannot hide its own latencies, from about four waves per SIMD the VALU
+// stays busy, and more rounds still shorten the per-token time a little (the
+// last round's tail is a smaller share).  The carry scan costs ~4 us plus a
+// per-carry term set by its traffic (or by its latency when there are few
+// channels); every extra launch ~4 us.
 constexpr int64_t kSimds = 1024;
-constexpr double kOutUs[7] = {0.0, 0.36, 0.241, 0.235, 0.206, 0.200, 0.192};   // by waves per SIMD
-constexpr double kCarryUs[7] = {0.0, 0.30, 0.211, 0.198, 0.169, 0.165, 0.157};
+constexpr int kMaxW = 12;
+constexpr double kOutUs[kMaxW + 1] = {0.0,   0.36,  0.241, 0.235, 0.206, 0.200, 0.192,
+                                      0.187, 0.187, 0.187, 0.180, 0.180, 0.175};   // by waves per SIMD
+constexpr double kCarryUs[kMaxW + 1] = {0.0,   0.30,  0.211, 0.198, 0.169, 0.165, 0.157,
+                                        0.151, 0.151, 0.151, 0.143, 0.143, 0.140};
 
 constexpr double kWaveSetupTokens = 6.0;     // per-wavefront prologue, in token equivalents
 
 double est_pass(int64_t waves, int64_t tokens, const double* per_token) {
     if (waves <= 0) return 0.0;
     const int64_t w = (waves + kSimds - 1) / kSimds;
-    return static_cast<double>(w) * (static_cast<double>(tokens) + kWaveSetupTokens) * per_token[w < 6 ? w : 6];
+    return static_cast<double>(w) * (static_cast<double>(tokens) + kWaveSetupTokens) * per_token[w < kMaxW ? w : kMaxW];
 }
 
 double est_plan(int64_t batch, int64_t D, int64_t L, int64_t len) {
