@@ -54,6 +54,16 @@ def test_plan_and_workspace():
         assert cl % 32 == 0 and nc == -(-l // cl) and nc >= 1
 
 
+def test_plan_choices_for_the_measured_shapes():
+    """The cost model picks what a --chunk-len sweep on the GPU measured fastest
+    (130M layer: 64 vs 32/96/128; 2.8B layer: 64 vs 96/128/192/256; 128k: 256 vs
+    512/1024), and the backward plan keeps 64-token chunks on the 130M layer."""
+    assert binding.plan(8, 2048, 1536, 1, 0) == (64, 32)
+    assert binding.plan(4, 2048, 5120, 1, 0) == (64, 32)
+    assert binding.plan(1, 131072, 2048, 1, 0) == (256, 512)
+    assert binding.bwd_plan(8, 2048, 1536, 1, 0) == (64, 32)
+
+
 def test_chunk_bytes_limit():
     """A chunk's rows are addressed with 32-bit offsets: at most 2 GiB per chunk (4 bytes per element)."""
     L = binding.lib()
