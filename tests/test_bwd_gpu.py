@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, assert_grads_close, gpu_bwd, log, oracle_bwd
+import oracle
+from gpu_util import TOL, assert_close, assert_grads_close, gpu_bwd, host64, log, oracle_bwd
 from selective_state_space_39_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +75,25 @@ def test_bwd_full_size_mamba130m_layer():
     log("oracle (channel strips) ...")
     ref = oracle_bwd(s, go, h0=False, strip=192)
     assert_grads_close(g, ref, TOL["bf16"], "bwd 130M layer")
+
+
+def test_bwd_full_size_mamba28b_layer_sampled_channels():
+    """The 2.8B-layer workload (4 x 2048 x 5120, bf16) at the automatic plan: the per-channel
+    gradients (dx, ddelta, dz, dA, dD, ddt_bias) of 64 sampled channels against the oracle run
+    on those channels alone (dB and dC sum over every channel: the 130M-layer case checks them
+    in full)."""
+    name = "mamba-2.8b-layer"
+    s = inputs.make_workload(name)
+    go = inputs.make_grad_outputs(4, 2048, 5120, io="bf16", seed=inputs.SCAN_WORKLOADS[name]["seed"],
+                                  with_dh_last=False)
+    log(f"full-size bwd plan {binding.bwd_plan(4, 2048, 5120, 1, 0)}")
+    g = gpu_bwd(s, go, h0=False)
+    ch = np.unique(np.concatenate([[0, 63, 64, 5119], np.random.default_rng([39, 4400]).choice(5120, 60, replace=False)]))
+    r = oracle.scan_bwd(s.x[:, :, ch], s.delta[:, :, ch], s.A[ch], s.B, s.C, s.Dskip[ch], s.dt_bias[ch],
+                        go.dout[:, :, ch], z=s.z[:, :, ch], io="bf16")
+    for k, axis in (("x", 2), ("delta", 2), ("z", 2), ("A", 0), ("Dskip", 0), ("dt_bias", 0)):
+        v = host64(g[k])
+        assert_close(v[:, :, ch] if axis == 2 else v[ch], r[k], TOL["bf16"], f"bwd 2.8B layer d{k} (sampled)")
 
 
 def test_bwd_errors_raise_before_launch():

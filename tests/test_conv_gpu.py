@@ -101,6 +101,35 @@ def test_conv_decode_step_matches_oracle(batch, D, io, K, gated):
         assert np.array_equal(host64(cs), oracle.decode(rcs, io)), "conv state must shift by one input exactly"
 
 
+def test_conv_decode_256x5120_chain_sampled():
+    """The decode-256x5120-conv workload (width 4): 8 chained steps on the full 256 x 5120
+    state in the bench's launch configuration; y, the state and the conv state of a
+    16 x 256 sample of (batch row, channel) pairs against the oracle's own float64 chain."""
+    batch, D, io = 256, 5120, "bf16"
+    A, Dskip, dt_bias, h0 = inputs.decode_params(batch, D)
+    cp = inputs.make_conv_params(batch, D, 4, io=io, seed=inputs.DECODE_WORKLOAD["seed"], with_init=True)
+    r = np.random.default_rng([39, 5600])
+    bsel = np.sort(np.concatenate([[0, batch - 1], r.choice(np.arange(1, batch - 1), 14, replace=False)]))
+    dsel = np.sort(np.concatenate([[0, 63, 64, D - 1], r.choice(np.arange(65, D - 1), 252, replace=False)]))
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    h, cs = f(h0), dev(cp.init, io)
+    tA, tD, tb, w, b = f(A), f(Dskip), f(dt_bias), f(cp.w), f(cp.b)
+    sub = lambda a: a[bsel][:, dsel]
+    hs = sub(h0).astype(np.float64)
+    css = cp.init[bsel][:, :, dsel]
+    for step in range(8):
+        tok = inputs.decode_token(step, batch, D)
+        y = binding.conv_state_update(h, cs, dev(tok.x, io), w, b, dev(tok.delta, io), tA, dev(tok.B, io),
+                                      dev(tok.C, io), tD, tb, z=dev(tok.z, io))
+        torch.cuda.synchronize()
+        ry, hs, css = oracle.conv_state_update(css, hs, sub(tok.x), cp.w[dsel], cp.b[dsel], sub(tok.delta), A[dsel],
+                                               tok.B[bsel], tok.C[bsel], Dskip[dsel], dt_bias[dsel], z=sub(tok.z),
+                                               io=io)
+        assert_close(sub(host64(y)), ry, TOL[io], f"conv decode step {step} y")
+        assert_close(sub(host64(h)), hs, TOL[io], f"conv decode step {step} h")
+        assert np.array_equal(host64(cs)[bsel][:, :, dsel], oracle.decode(css, io)), f"conv state at step {step}"
+
+
 def test_conv_prompt_then_decode_equals_scan():
     """Serving a stream: conv scan over a prompt, then chained conv decode steps from its
     (h_last, conv_last), equal the conv scan over the whole sequence (oracle)."""
