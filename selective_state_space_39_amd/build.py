@@ -56,8 +56,27 @@ def build(asm_dir: str | None = None, quiet: bool = False) -> str:
     return LIB
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "c_abi", "scan_demo.cpp")
+DEMO = os.path.join(ROOT, "tests", "c_abi", "scan_demo")
+
+
+def build_demo() -> str:
+    """The C-ABI example consumer the tests run (plain C++ and the HIP runtime,
+    no Python): linked against the in-tree library, found through an rpath
+    relative to the binary, so the tree can move."""
+    rpath = "$ORIGIN/" + os.path.relpath(HERE, os.path.dirname(DEMO))
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wall", f"--offload-arch={ARCH}", "-I", INCLUDE, DEMO_SRC, "-o", DEMO + ".tmp",
+           "-L", HERE, "-lssm_scan", f"-Wl,-rpath,{rpath}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    os.replace(DEMO + ".tmp", DEMO)
+    return DEMO
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", default=None)
     args = ap.parse_args()
     print(build(args.asm))
+    print(build_demo())
