@@ -55,13 +55,16 @@ def test_plan_and_workspace():
 
 
 def test_plan_choices_for_the_measured_shapes():
-    """The cost model picks what a --chunk-len sweep on the GPU measured fastest
+    """The cost model picks what a chunk-length sweep on the GPU measured fastest
     (130M layer: 64 vs 32/96/128; 2.8B layer: 64 vs 96/128/192/256; 128k: 256 vs
-    512/1024), and the backward plan keeps 64-token chunks on the 130M layer."""
+    512/1024; 1 x 2048 x 768: 32 vs 64/128), and the backward plan keeps
+    64-token chunks on the 130M layer."""
     assert binding.plan(8, 2048, 1536, 1, 0) == (64, 32)
     assert binding.plan(4, 2048, 5120, 1, 0) == (64, 32)
     assert binding.plan(1, 131072, 2048, 1, 0) == (256, 512)
     assert binding.bwd_plan(8, 2048, 1536, 1, 0) == (64, 32)
+    # few channels (12 wavefronts per chunk): many short chunks; measured 36 us at 32 vs 50 us at 64
+    assert binding.plan(1, 2048, 768, 1, 0) == (32, 64)
 
 
 def test_chunk_bytes_limit():
