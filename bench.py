@@ -53,7 +53,9 @@ WORKLOADS = {"mamba-130m-layer": ("scan", "mamba-130m-layer"), "mamba-2.8b-layer
              "long-context-128k": ("scan", "long-context-128k"), "decode-256x5120": ("decode", None),
              "mamba-130m-layer-bwd": ("bwd", "mamba-130m-layer"), "mamba-2.8b-layer-bwd": ("bwd", "mamba-2.8b-layer"),
              "mamba-130m-layer-conv": ("conv", "mamba-130m-layer"), "decode-256x5120-conv": ("decode", None),
-             "mamba2-2.7b-layer": ("ssd", None)}
+             "mamba2-2.7b-layer": ("ssd", "mamba2-2.7b-layer"),
+             "mamba2-2.7b-layer-n64": ("ssd", "mamba2-2.7b-layer-n64"),
+             "mamba2-2.7b-layer-n256": ("ssd", "mamba2-2.7b-layer-n256")}
 PEAK_BF16_TFLOPS = 2500.0           # dense bf16 matrix-core peak
 CONV_K = 4                          # width of the fused local convolution in the -conv workloads
 CONV_SLOTS = 14                     # per element: 4 FMA + silu (exp 4, rcp 4, add, mul)
@@ -427,11 +429,12 @@ def ssd_flops(batch, L, H, P, N, Q=64):
     return batch * chunks * H * (Q * Q * P + 2 * Q * N * P + 2 * P * Q * N)
 
 
-def bench_ssd(args):
-    """The SSD (Mamba-2 style) layer on the 2.7B-layer shape: 8 x 2048 tokens, 80 heads of 64, N = 128."""
+def bench_ssd(args, name):
+    """The SSD (Mamba-2 style) layer on the 2.7B-layer shape: 8 x 2048 tokens, 80 heads of 64, N = 128
+    (or 64, 256 for the -n64, -n256 workloads)."""
     import torch
     from selective_state_space_39_amd import binding, inputs
-    w = inputs.SSD_WORKLOAD
+    w = inputs.SSD_WORKLOADS[name]
     s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=w["seed"])
     batch, L, H, P, N = s.shape
     dev = torch.device("cuda:0")
@@ -479,7 +482,7 @@ def bench_ssd(args):
            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "mamba2-2.7b-layer ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
+           "config": {"workload": f"{name} ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
                       "io": "bf16", "state": "f32", "gated": True, "chunk": 64},
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, "ssd_chunked"),
@@ -540,7 +543,7 @@ def main():
 
     kind, name = WORKLOADS[args.workload]
     if kind == "ssd":
-        return bench_ssd(args)
+        return bench_ssd(args, name)
     if kind == "decode":
         return bench_decode(args)
     if kind == "bwd":

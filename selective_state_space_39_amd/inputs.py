@@ -273,6 +273,11 @@ class SsdInputs:
 
 
 SSD_WORKLOAD = dict(name="mamba2-2.7b-layer", batch=8, L=2048, H=80, P=64, N=128, io="bf16", seed=(SEED_ROOT, 6))
+# The same layer at the two other state sizes the kernels are built for.
+SSD_WORKLOADS = {w["name"]: w for w in (
+    SSD_WORKLOAD,
+    dict(SSD_WORKLOAD, name="mamba2-2.7b-layer-n64", N=64, seed=(SEED_ROOT, 10)),
+    dict(SSD_WORKLOAD, name="mamba2-2.7b-layer-n256", N=256, seed=(SEED_ROOT, 11)))}
 
 
 def make_ssd_inputs(batch: int, L: int, H: int, P: int = 64, N: int = 128, io: str = "bf16",

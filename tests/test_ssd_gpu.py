@@ -51,15 +51,18 @@ def test_ssd_deterministic():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
-def test_ssd_full_size_sampled_heads():
-    """The 2.7B-layer workload (8 x 2048, 80 heads of 64, N = 128) on 3 sampled heads."""
-    w = inputs.SSD_WORKLOAD
-    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=(39, 6))
+@pytest.mark.parametrize("name", sorted(inputs.SSD_WORKLOADS))
+def test_ssd_full_size_sampled_heads(name):
+    """The 2.7B-layer workload (8 x 2048, 80 heads of 64; N = 128, and 64, 256) on 3 sampled heads, with
+    the bench's seed."""
+    w = inputs.SSD_WORKLOADS[name]
+    log(f"ssd full size {name}: N {w['N']}")
+    s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=w["seed"])
     y, h = gpu_ssd(s, h0=False)
     heads = [0, 41, 79]
     ry, rh = oracle_ssd(s, heads=heads, h0=False)
-    assert_close(host64(y)[:, :, heads], ry, TOL["bf16"], "ssd 2.7B layer y (3 heads)")
-    assert_close(host64(h)[:, heads], rh, TOL["bf16"], "ssd 2.7B layer h_L (3 heads)")
+    assert_close(host64(y)[:, :, heads], ry, TOL["bf16"], f"ssd {name} y (3 heads)")
+    assert_close(host64(h)[:, heads], rh, TOL["bf16"], f"ssd {name} h_L (3 heads)")
 
 
 def test_ssd_errors():
