@@ -239,3 +239,61 @@ def test_side_stream():
                                   h0=t["h0"], chunk_len=64)
     side.synchronize()
     assert torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+def test_concurrent_host_threads_on_own_streams():
+    """Four host threads, each on a stream of its own, interleave scans, decode steps and SSD layers on their own
+    inputs; every result equals, bit for bit, the same call made alone.  The library keeps no per-call state
+    outside its arguments (the error string is per thread), so calls on different streams do not interact."""
+    import threading
+
+    cases = []
+    for k in range(4):
+        s = inputs.make_scan_inputs(2, 333 + 40 * k, 96 + 32 * k, io="bf16", seed=(39, 2100 + k), with_h0=True)
+        q = inputs.make_ssd_inputs(1, 150 + 30 * k, 3, N=(64, 128, 256, 128)[k], seed=(39, 2110 + k), with_h0=True)
+        A, Dskip, dt_bias, h0 = inputs.decode_params(8, 256, seed=(39, 2120 + k))
+        tok = inputs.decode_token(0, 8, 256, io="bf16", seed_root=(39, 2120 + k))
+        cases.append((_dev_all(s), q, (f32dev(A), f32dev(Dskip), f32dev(dt_bias), h0, tok)))
+
+    def one_round(case):
+        t, q, (A, Dskip, dt_bias, h0, tok) = case
+        y, h = binding.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"], z=t["z"],
+                                h0=t["h0"])
+        qd = {k: dev(getattr(q, k), "bf16") for k in ("x", "delta", "z", "B", "C")}
+        qy, qh = binding.ssd_fwd(qd["x"], qd["delta"], f32dev(q.A), qd["B"], qd["C"], f32dev(q.Dskip),
+                                 f32dev(q.dt_bias), z=qd["z"], h0=f32dev(q.h0))
+        hs = f32dev(h0)
+        dy = binding.state_update(hs, dev(tok.x, "bf16"), dev(tok.delta, "bf16"), A, dev(tok.B, "bf16"),
+                                  dev(tok.C, "bf16"), Dskip, dt_bias, z=dev(tok.z, "bf16"))
+        return [y, h, qy, qh, dy, hs]
+
+    alone = []
+    for case in cases:
+        alone.append(one_round(case))
+        torch.cuda.synchronize()
+
+    got, errors = [None] * len(cases), []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(5):
+                    out = one_round(cases[i])
+                st.synchronize()
+            got[i] = out
+        except Exception as e:      # reported below, on the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    names = ["scan y", "scan h_L", "ssd y", "ssd h_L", "decode y", "decode h"]
+    for i in range(len(cases)):
+        for n, a, b in zip(names, alone[i], got[i]):
+            assert torch.equal(a, b), f"thread {i}: {n} differs from the call made alone"
+    log("4 threads x 5 rounds of scan, SSD and decode calls: all equal to the calls made alone")
