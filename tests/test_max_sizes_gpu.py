@@ -79,3 +79,41 @@ def test_ssd_batch_row_at_the_32bit_offset_limit():
     for k in (0, H - 1):
         assert_close(host64(y[:, :, k:k + 1].contiguous()), ry, TOL["bf16"], f"ssd y, head {k}")
         assert_close(host64(h[:, k:k + 1].contiguous()), rh, TOL["bf16"], f"ssd h_L, head {k}")
+
+
+def test_backward_chunk_at_the_32bit_offset_limit():
+    """The backward with the same longest fp32 chunk (32736 tokens of 16384 channels, two batch rows, 36 GiB of
+    sub-chunk checkpoints in the workspace).  Per-channel gradients are bit-equal across tiles; dB and dC sum
+    over all 16384 channels, i.e. 256 times the small problem's sums."""
+    import oracle
+    batch, L, D = 2, 33736, 16384
+    cl = (2 ** 31 - 1) // (4 * D) // 32 * 32
+    assert binding.bwd_plan(batch, L, D, binding.SSM_F32, cl) == (cl, 2)
+    s = inputs.make_scan_inputs(batch, L, BASE, io="f32", seed=(39, 2220), with_h0=True, A_random=True)
+    go = inputs.make_grad_outputs(batch, L, BASE, io="f32", seed=(39, 2220), with_dh_last=True)
+    reps = D // BASE
+    log(f"backward {batch} x {L} x {D} fp32, chunk {cl}: workspace "
+        f"{binding.lib().ssm_scan_bwd_workspace_bytes(batch, L, D, 16, binding.SSM_F32, cl) / 2 ** 30:.1f} GiB")
+    x, dl, z, dout = (_tiled_dev(a, reps, 2) for a in (s.x, s.delta, s.z, go.dout))
+    A, Dk, bias = (_tiled_dev(a, reps, 0) for a in (s.A, s.Dskip, s.dt_bias))
+    h0, dh_last = (_tiled_dev(a, reps, 1) for a in (s.h0, go.dh_last))
+    g = binding.scan_bwd(x, dl, A, _tiled_dev(s.B, 1, 0), _tiled_dev(s.C, 1, 0), Dk, bias, dout, z=z, h0=h0,
+                         dh_last=dh_last, chunk_len=cl)
+    torch.cuda.synchronize()
+    del x, dl, z, dout
+    ref = oracle.scan_bwd(s.x, s.delta, s.A, s.B, s.C, s.Dskip, s.dt_bias, go.dout, z=s.z, h0=s.h0,
+                          dh_last=go.dh_last, io=s.io)
+    per_element = (batch, L, reps, BASE)                # tile axis 2
+    for k, shape, ax in (("x", per_element, 2), ("delta", per_element, 2), ("z", per_element, 2),
+                         ("h0", (batch, reps, BASE, 16), 1)):
+        t = g[k].view(shape)
+        assert bool((t == t.narrow(ax, 0, 1)).all()), f"a channel tile of d{k} differs from the first"
+        for j in (0, reps - 1):
+            assert_close(host64(t.select(ax, j).contiguous()), ref[k], TOL["f32"], f"d{k}, tile {j}")
+    for k, n in (("A", 16), ("Dskip", 0), ("dt_bias", 0)):
+        t = g[k].view(reps, BASE, n) if n else g[k].view(reps, BASE)
+        assert bool((t == t[:1]).all()), f"a channel tile of d{k} differs from the first"
+        for j in (0, reps - 1):
+            assert_close(host64(t[j].contiguous()), ref[k], TOL["f32"], f"d{k}, tile {j}")
+    for k in ("B", "C"):
+        assert_close(host64(g[k]) / reps, ref[k], TOL["f32"], f"d{k} / {reps}")
