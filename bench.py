@@ -435,6 +435,9 @@ def bench_ssd(args, name):
     import torch
     from selective_state_space_39_amd import binding, inputs
     w = inputs.SSD_WORKLOADS[name]
+    if args.heads:
+        w = dict(w, H=args.heads)
+        name = f"{name} with {args.heads} heads"
     s = inputs.make_ssd_inputs(w["batch"], w["L"], w["H"], w["P"], w["N"], seed=w["seed"])
     batch, L, H, P, N = s.shape
     dev = torch.device("cuda:0")
@@ -485,7 +488,7 @@ def bench_ssd(args, name):
            "config": {"workload": f"{name} ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
                       "io": "bf16", "state": "f32", "gated": True, "chunk": 64},
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, "ssd_chunked"),
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None if args.heads else measured_traffic(args.workload, "ssd_chunked"),
                         "kernel": "ssd_chunked", "avg_launch_ms": round(avg_ms, 5),
                         "work": f"{abytes} algorithmic bytes per launch (x, z read, y written, delta, B, C)"},
            "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": PEAK_BF16_TFLOPS,
@@ -515,6 +518,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mamba-130m-layer", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
+    ap.add_argument("--heads", type=int, default=0,
+                    help="SSD workloads: run the layer with this many heads instead (an occupancy sweep; the "
+                         "line's config then names the changed shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the cache-flushed single steps (kernel traces then cover the timed loops only)")
