@@ -56,6 +56,35 @@ def test_scan_chunk_at_the_32bit_offset_limit():
         assert_close(host64(ht[:, k].contiguous()), rh, TOL["f32"], f"h_L, tile {k}")
 
 
+
+def test_conv_scan_chunk_at_the_32bit_offset_limit():
+    """The scan fed by the width-4 convolution at the same limit: the second chunk's window starts from the
+    three rows before it, 2 GiB into each batch row."""
+    import oracle
+    batch, L, D, K = 2, 33736, 16384, 4
+    cl = (2 ** 31 - 1) // (4 * D) // 32 * 32
+    s = inputs.make_scan_inputs(batch, L, BASE, io="f32", seed=(39, 2230), with_h0=True)
+    cp = inputs.make_conv_params(batch, BASE, K, io="f32", seed=(39, 2230), with_init=True)
+    reps = D // BASE
+    log(f"conv scan {batch} x {L} x {D} fp32, K {K}, chunk {cl}")
+    xin, dl, z = (_tiled_dev(a, reps, 2) for a in (s.x, s.delta, s.z))
+    A, Dk, bias, cb = (_tiled_dev(a, reps, 0) for a in (s.A, s.Dskip, s.dt_bias, cp.b))
+    cw = _tiled_dev(cp.w, reps, 0)
+    h0, init = _tiled_dev(s.h0, reps, 1), _tiled_dev(cp.init, reps, 2)
+    y, h, last = binding.conv_scan_fwd(xin, cw, cb, dl, A, _tiled_dev(s.B, 1, 0), _tiled_dev(s.C, 1, 0), Dk, bias,
+                                       z=z, h0=h0, conv_init=init, chunk_len=cl, return_conv_last=True)
+    torch.cuda.synchronize()
+    assert torch.equal(last, xin[:, L - (K - 1):]), "conv_last is not the last K - 1 inputs"
+    del xin, dl, z
+    yt, ht = y.view(batch, L, reps, BASE), h.view(batch, reps, BASE, 16)
+    assert bool((yt == yt[:, :, :1]).all()), "a channel tile of y differs from the first"
+    assert bool((ht == ht[:, :1]).all()), "a channel tile of h_L differs from the first"
+    ry, rh = oracle.conv_scan_fwd(s.x, cp.w, cp.b, s.delta, s.A, s.B, s.C, s.Dskip, s.dt_bias, z=s.z, h0=s.h0,
+                                  conv_init=cp.init, io=s.io)
+    for k in (0, reps - 1):
+        assert_close(host64(yt[:, :, k].contiguous()), ry, TOL["f32"], f"conv y, tile {k}")
+        assert_close(host64(ht[:, k].contiguous()), rh, TOL["f32"], f"conv h_L, tile {k}")
+
 def test_ssd_batch_row_at_the_32bit_offset_limit():
     """SSD layer, 80 heads, N = 128, L = 209715: one batch row's x, z and y are 2 147 481 600 bytes each, the
     largest L the library accepts at 80 heads (one more token is refused)."""
