@@ -360,3 +360,79 @@ def test_last_error_is_per_thread():
     t2 = threading.Thread(target=worker, args=("dtype", (1, 10, 8, 16, 7, 0)))  # bad dtype
     t1.start(); t2.start(); t1.join(); t2.join()
     assert "N = 8" in out["n"] and "dtype" in out["dtype"]
+
+
+def _size_ints():
+    from hypothesis import strategies as st
+    return st.one_of(st.integers(-3, 300), st.integers(1, 1 << 20), st.integers(-(1 << 62), 1 << 62),
+                     st.sampled_from([0, 1, 31, 32, 33, 64, 65535, 65536, 1 << 31, (1 << 31) - 1, 1 << 40]))
+
+
+def _check_plan(fn, batch, L, D, dtype, chunk):
+    cl, nc = ctypes.c_int64(-7), ctypes.c_int64(-7)
+    rc = fn(batch, L, D, 16, dtype, chunk, ctypes.byref(cl), ctypes.byref(nc))
+    return rc, cl.value, nc.value
+
+
+def test_host_queries_never_misbehave():
+    """Random (including negative, zero and huge) shapes through every host-only query: each call either
+    succeeds with a consistent plan and workspace or returns one of the header's error codes with a message;
+    a successful plan covers L with whole chunks whose rows fit 32-bit offsets."""
+    from hypothesis import given, settings, strategies as st
+    L = binding.lib()
+    errors = {E_NULL, E_SHAPE, E_N, E_DTYPE, E_ALIGN, E_WS, E_ALIAS}
+
+    @settings(max_examples=400, deadline=None)
+    @given(batch=_size_ints(), length=_size_ints(), D=_size_ints(), N=st.sampled_from([16, 8, 0, -1, 64, 128, 256]),
+           dtype=st.sampled_from([0, 1, 2, -1]), chunk=_size_ints())
+    def run(batch, length, D, N, dtype, chunk):
+        for ws_fn, plan_fn in ((L.ssm_scan_fwd_workspace_bytes, L.ssm_scan_fwd_plan),
+                               (L.ssm_scan_bwd_workspace_bytes, L.ssm_scan_bwd_plan)):
+            ws = ws_fn(batch, length, D, N, dtype, chunk)
+            if ws < 0:
+                assert ws in errors and L.ssm_last_error(), (batch, length, D, N, dtype, chunk, ws)
+                continue
+            assert N == 16 and dtype in (0, 1) and batch >= 1 and length >= 1 and D >= 1
+            rc, cl, nc = _check_plan(plan_fn, batch, length, D, dtype, chunk)
+            assert rc == OK, (batch, length, D, dtype, chunk, rc)
+            assert cl >= 1 and nc == -(-length // cl) and (nc == 1 or cl % 32 == 0)
+            assert chunk <= 0 or cl == chunk or (nc == 1 and cl >= length)
+            assert nc == 1 or cl * D * 4 <= (1 << 31) - 1
+            carries = (nc - 1) * batch * D * 17 * 4
+            assert ws >= carries
+        ws = L.ssm_ssd_fwd_workspace_bytes(batch, length, D, 64, N, dtype)
+        if ws < 0:
+            assert ws in errors and L.ssm_last_error()
+        else:
+            assert N in (64, 128, 256) and dtype == 1 and ws == batch * -(-length // 64) * 64 * 64 * 2
+
+    run()
+
+
+def test_plans_of_plausible_shapes_are_consistent():
+    """Shapes a caller would pass (the automatic plan or an explicit multiple of 32): the plan covers L with
+    whole chunks, honours an explicit chunk length, keeps a chunk's rows within 32-bit offsets, and the
+    workspace holds the (n - 1) carries of 17 floats per (batch row, channel)."""
+    from hypothesis import given, settings, strategies as st
+    L = binding.lib()
+
+    @settings(max_examples=300, deadline=None)
+    @given(batch=st.integers(1, 64), length=st.integers(1, 300000), D=st.integers(1, 20000),
+           dtype=st.sampled_from([0, 1]), chunk=st.one_of(st.just(0), st.integers(1, 2000).map(lambda k: 32 * k)))
+    def run(batch, length, D, dtype, chunk):
+        for ws_fn, plan_fn in ((L.ssm_scan_fwd_workspace_bytes, L.ssm_scan_fwd_plan),
+                               (L.ssm_scan_bwd_workspace_bytes, L.ssm_scan_bwd_plan)):
+            ws = ws_fn(batch, length, D, 16, dtype, chunk)
+            rc, cl, nc = _check_plan(plan_fn, batch, length, D, dtype, chunk)
+            if chunk and chunk * D * 4 > (1 << 31) - 1:
+                assert ws == E_SHAPE and rc == E_SHAPE           # an explicit chunk beyond the offset limit
+                continue
+            assert ws >= 0 and rc == OK, (batch, length, D, dtype, chunk, ws, rc)
+            assert cl >= 1 and nc == -(-length // cl) and (nc == 1 or cl % 32 == 0)
+            assert chunk == 0 or cl == chunk or (nc == 1 and cl >= length)
+            assert nc == 1 or cl * D * 4 <= (1 << 31) - 1
+            assert ws >= (nc - 1) * batch * D * 17 * 4
+            if plan_fn is L.ssm_scan_fwd_plan:
+                assert (ws == 0) == (nc == 1)
+
+    run()
