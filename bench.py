@@ -55,7 +55,8 @@ WORKLOADS = {"mamba-130m-layer": ("scan", "mamba-130m-layer"), "mamba-2.8b-layer
              "mamba-130m-layer-conv": ("conv", "mamba-130m-layer"), "decode-256x5120-conv": ("decode", None),
              "mamba2-2.7b-layer": ("ssd", "mamba2-2.7b-layer"),
              "mamba2-2.7b-layer-n64": ("ssd", "mamba2-2.7b-layer-n64"),
-             "mamba2-2.7b-layer-n256": ("ssd", "mamba2-2.7b-layer-n256")}
+             "mamba2-2.7b-layer-n256": ("ssd", "mamba2-2.7b-layer-n256"),
+             "mamba2-long-context-128k": ("ssd", "mamba2-long-context-128k")}
 PEAK_BF16_TFLOPS = 2500.0           # dense bf16 matrix-core peak
 CONV_K = 4                          # width of the fused local convolution in the -conv workloads
 CONV_SLOTS = 14                     # per element: 4 FMA + silu (exp 4, rcp 4, add, mul)
@@ -486,7 +487,8 @@ def bench_ssd(args, name):
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"{name} ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
-                      "io": "bf16", "state": "f32", "gated": True, "chunk": 64},
+                      "io": "bf16", "state": "f32", "gated": True, "chunk": 64,
+                      "segments": binding.ssd_plan(batch, L, H, N, P)[0]},
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None if args.heads else measured_traffic(args.workload, "ssd_chunked"),
                         "kernel": "ssd_chunked", "avg_launch_ms": round(avg_ms, 5),

@@ -283,9 +283,17 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z,
  *   workspace at least ssm_ssd_fwd_workspace_bytes(...) bytes of device
  *             memory, 16-byte aligned, owned by the caller, contents ignored;
  *             it receives C_t . B_i of every chunk (bf16, no head in it), which
- *             all heads of a batch row share.  It must not overlap any argument
- *             and must not be used by another call until this one's work on
- *             the stream is done.
+ *             all heads of a batch row share, and, when the sequences are cut
+ *             into segments (see ssm_ssd_fwd_plan), each segment's fp32 end
+ *             state and starting state.  It must not overlap any argument and
+ *             must not be used by another call until this one's work on the
+ *             stream is done.
+ * When batch * H sequences are too few to fill the GPU, each sequence is cut
+ * into segments of whole chunks walked in parallel: a first pass leaves each
+ * segment's end state from zero and its total decay, an in-order fold turns
+ * them into every segment's starting state (the combine of "Mamba", "Scan
+ * View", with a scalar decay per head), and the layer then runs per segment.
+ * The result is the same function up to rounding order.
  * io_dtype must be SSM_BF16 (SSM_ERR_DTYPE otherwise); N other than 64, 128
  * or 256 is SSM_ERR_N; P other than 64 is SSM_ERR_SHAPE; a missing or small
  * workspace is SSM_ERR_WORKSPACE.
@@ -298,9 +306,17 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z,
                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes ssm_ssd_fwd needs: batch * ceil(L / 64) * 8192.  Negative
- * ssm_status for an invalid shape.  Host-only; touches no device. */
+/* Workspace bytes ssm_ssd_fwd needs: batch * ceil(L / 64) * 8192, plus
+ * batch * H * (n_segments - 1) * (64 * N + 1) * 4 when the plan below cuts the
+ * sequences into n_segments > 1 segments.  Negative ssm_status for an invalid
+ * shape.  Host-only; touches no device. */
 int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype);
+
+/* The segments ssm_ssd_fwd cuts each sequence into (1 = walked whole) and the
+ * chunks of 64 tokens per segment (the last segment may be shorter).  Errors
+ * as ssm_ssd_fwd_workspace_bytes; NULL outputs are SSM_ERR_NULL.  Host-only. */
+int ssm_ssd_fwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype,
+                     int64_t* n_segments, int64_t* segment_chunks);
 
 /*
  * Per-kernel timing, for measurement tools; not needed to compute anything.

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_ssd_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i64, i32, vp, i64, vp]
     L.ssm_ssd_fwd_workspace_bytes.restype = i64
     L.ssm_ssd_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.ssm_ssd_fwd_plan.restype = i32
+    L.ssm_ssd_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     L.ssm_scan_bwd_plan.restype = i32
@@ -348,8 +350,16 @@ def conv_state_update(h, conv_state, xin, conv_w, conv_b, delta, A, B, C, D, dt_
     return y
 
 
+def ssd_plan(batch: int, L: int, H: int, N: int, P: int = 64) -> Tuple[int, int]:
+    """(segments per sequence, chunks of 64 tokens per segment) ssd_fwd uses for this shape."""
+    ns, sc = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ssm_ssd_fwd_plan(batch, L, H, P, N, SSM_BF16, ctypes.byref(ns), ctypes.byref(sc)))
+    return ns.value, sc.value
+
+
 def ssd_workspace_bytes(batch: int, L: int, H: int, N: int, P: int = 64) -> int:
-    """Device bytes ssd_fwd needs as workspace (the per-chunk C . B products)."""
+    """Device bytes ssd_fwd needs as workspace (the per-chunk C . B products, and the segment states when
+    the sequences are cut into segments)."""
     n = lib().ssm_ssd_fwd_workspace_bytes(batch, L, H, P, N, SSM_BF16)
     if n < 0:
         _check(n)

@@ -297,7 +297,13 @@ __device__ __forceinline__ void publish_state(Smem<N>& sm, const f32x4 (&st)[N /
             make_uint2(pack2(st[nb][0], st[nb][1]), pack2(st[nb][2], st[nb][3]));
 }
 
-template <int N, bool GATED>
+// LOCAL = false: the layer itself, each workgroup walking one segment of one
+// (batch row, head) sequence from its starting state (the caller's h0 for
+// segment 0, the fold's result for the others) and writing its outputs.
+// LOCAL = true: the first pass of a segmented layer, each workgroup walking
+// segment k < n_seg - 1 from a zero state with no outputs and leaving its end
+// state and its total decay in the workspace.
+template <int N, bool GATED, bool LOCAL>
 __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdArgs a) {
     constexpr int NB = N / 16;            // 16-row blocks of the state's n
     constexpr int KS = N / 32;            // k-steps of a product over n
@@ -308,17 +314,22 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
     const int l = tid & 63, r = l & 15, q = l >> 4;
     const int tw = 16 * w + r;            // this lane's token inside a chunk
     const int nks = w >= 2 ? 2 : 1;       // k-steps of 32 tokens that reach token 16w + 15
-    // (batch row, head): the heads of one batch row stay on one XCD (shared B, C, G rows in its L2)
-    const int64_t units = a.batch * a.H;
+    // (batch row, segment, head), head fastest: the heads of one batch row and
+    // segment stay on one XCD (shared B, C, G rows in its L2)
+    const int64_t nseg = LOCAL ? a.n_seg - 1 : a.n_seg;
+    const int64_t units = a.batch * nseg * a.H;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (u % 8) * (units / 8) + u / 8;
-    const int64_t b = u / a.H, h = u % a.H;
+    const int64_t h = u % a.H, seg = (u / a.H) % nseg, b = u / (a.H * nseg);
     const float A = a.A[h], bias = a.dt_bias[h], Dd = a.Dskip[h];
+    const int64_t nslot = a.n_seg - 1;    // segment states per sequence in the workspace
 
     // This wavefront owns channels p = 16 w .. 16 w + 15 of the state: tiles
     // state^T[n-block nb][p-block w], lane slot j = state^T[16 nb + 4q + j][16 w + r].
     f32x4 st[NB];
-    const float* h0 = a.h0 ? a.h0 + (b * a.H + h) * kP * N : nullptr;
+    const float* h0 = LOCAL ? nullptr
+                      : seg == 0 ? (a.h0 ? a.h0 + (b * a.H + h) * kP * N : nullptr)
+                                 : a.seg_state + ((b * a.H + h) * nslot + seg - 1) * kP * N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         if (h0) {
@@ -328,9 +339,12 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
             st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    publish_state<N>(sm, st, w);
+    if constexpr (!LOCAL) publish_state<N>(sm, st, w);
 
     const int nchunks = static_cast<int>((a.L + kQ - 1) / kQ);
+    const int c_begin = static_cast<int>(seg * a.seg_chunks);
+    const int c_end = c_begin + a.seg_chunks < nchunks ? static_cast<int>(c_begin + a.seg_chunks) : nchunks;
+    float decay = 0.0f;                   // log2 of the segment's total decay (LOCAL)
     SeqIO io;
     {
         const int64_t xoff = (b * a.L * a.H + h) * kP;                       // first element of the sequence
@@ -349,12 +363,14 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
     }
     StageRegs<N> sr;
     OwnRegs<N> own;
-    load_stage<N>(io, 0, w, sr);
-    load_cg<N>(io, 0, 0, w, own);
-    if constexpr (GATED) load_z<N>(io, 0, w, own);
+    load_stage<N>(io, c_begin * kQ, w, sr);
+    if constexpr (!LOCAL) {
+        load_cg<N>(io, c_begin, c_begin * kQ, w, own);
+        if constexpr (GATED) load_z<N>(io, c_begin * kQ, w, own);
+    }
     const uint32_t vrow = row_off(io, w);
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * kQ;
         const int nt = static_cast<int>(a.L - t0 < kQ ? a.L - t0 : kQ);
         stage_chunk<N>(sm, sr, nt, A, bias, w);
@@ -362,8 +378,36 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
         // Prefetches are unconditional (the last chunk reloads itself): with no
         // branch around them the compiler waits on each load by its exact
         // position in the in-order memory counter instead of draining it.
-        const int cn = c + 1 < nchunks ? c + 1 : c, t1 = cn * kQ;
+        const int cn = c + 1 < c_end ? c + 1 : c, t1 = cn * kQ;
         load_stage<N>(io, t1, w, sr);
+        if constexpr (LOCAL) {
+            // state update only: state^T = exp(S_end) state^T + B^T (W x)
+            const float s_end = sm.S2[kQ - 1];
+            decay += s_end;
+            const float dec = __builtin_amdgcn_exp2f(s_end);
+            bf16x8 xw[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int i0 = 32 * ks + 8 * q;
+                const bf16x8 xv = opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, i0, 16 * w);
+                const float4 wa = *reinterpret_cast<const float4*>(&sm.Wt[i0]);
+                const float4 wb = *reinterpret_cast<const float4*>(&sm.Wt[i0 + 4]);
+                const float wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(xv[j]) * wi[j];
+                xw[ks] = pack8(v);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 sv = st[nb] * dec;
+                sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw[0], sv);
+                sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw[1], sv);
+                st[nb] = sv;
+            }
+            __syncthreads();                           // every read of Xs, Bs of this chunk is done
+            continue;
+        }
 
         // M^T as the B operand of y^T: lane (r, q) holds M[t = 16w + r][i = 32ks + 8q .. +7]
         const float s2t = sm.S2[tw];
@@ -462,12 +506,59 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
         if constexpr (GATED) load_z<N>(io, t1, w, own);
         publish_state<N>(sm, st, w);                   // after this wavefront's staging reads (same rows)
     }
-    if (a.h_last) {
+    if constexpr (LOCAL) {
+        float* hs = a.seg_state + ((b * a.H + h) * nslot + seg) * kP * N;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<float4*>(hs + (16 * w + r) * N + 16 * nb + 4 * q) =
+                make_float4(st[nb][0], st[nb][1], st[nb][2], st[nb][3]);
+        if (tid == 0) a.seg_decay[(b * a.H + h) * nslot + seg] = decay;
+        return;
+    }
+    if (a.h_last && seg == a.n_seg - 1) {
         float* hl = a.h_last + (b * a.H + h) * kP * N;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             *reinterpret_cast<float4*>(hl + (16 * w + r) * N + 16 * nb + 4 * q) =
                 make_float4(st[nb][0], st[nb][1], st[nb][2], st[nb][3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ssd_seg_fold: the starting state of every segment after the first, in
+// order: start(k + 1) = 2^decay(k) start(k) + local(k), start(0) = h0 (or
+// zero), written over local(k).  One workgroup per (batch row, head); each
+// thread carries kPieces float4 of the 64 x N state, and the next segment's
+// pieces are loaded before this segment's are stored.
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_seg_fold(SsdArgs a) {
+    constexpr int kPieces = kP * N / 4 / kThreads;       // 4, 8 or 16
+    const int64_t bh = blockIdx.x, nslot = a.n_seg - 1;
+    const int tid = threadIdx.x;
+    float4 v[kPieces], nxt[kPieces];
+    const float4* h0 = a.h0 ? reinterpret_cast<const float4*>(a.h0 + bh * kP * N) : nullptr;
+    float4* base = reinterpret_cast<float4*>(a.seg_state + bh * nslot * kP * N);
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+        v[k] = h0 ? h0[tid + kThreads * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+        nxt[k] = base[tid + kThreads * k];
+    }
+    for (int64_t sl = 0; sl < nslot; ++sl) {
+        const float d = __builtin_amdgcn_exp2f(a.seg_decay[bh * nslot + sl]);
+        float4* cur = base + sl * (kP * N / 4);
+        float4 loc[kPieces];
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) loc[k] = nxt[k];
+        const int64_t sn = sl + 1 < nslot ? sl + 1 : sl;   // the last slot reloads itself
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) nxt[k] = base[sn * (kP * N / 4) + tid + kThreads * k];
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) {
+            v[k] = make_float4(fmaf(d, v[k].x, loc[k].x), fmaf(d, v[k].y, loc[k].y), fmaf(d, v[k].z, loc[k].z),
+                               fmaf(d, v[k].w, loc[k].w));
+            cur[tid + kThreads * k] = v[k];
+        }
     }
 }
 
@@ -477,16 +568,60 @@ using namespace ssd;
 
 int64_t ssd_gram_bytes(int64_t batch, int64_t L) { return batch * ((L + kQ - 1) / kQ) * kQ * kQ * 2; }
 
+// Workgroups of ssd_chunked resident per CU (LDS and VGPRs): 3 up to N = 128,
+// 2 at N = 256.  Sequences (batch rows x heads) are cut into as many segments
+// as keep every (sequence, segment) workgroup resident at once, never more:
+// a CU's throughput, not one workgroup's chain, bounds the walk from two
+// workgroups per CU on.
+constexpr int64_t kCUs = 256;
+// A segment spans at least this many chunks (1024 tokens): its first pass and
+// the fold then add little to the walk itself.
+constexpr int64_t kMinSegChunks = 16;
+
+void ssd_segments(int64_t batch, int64_t L, int64_t H, int64_t N, int64_t* n_seg, int64_t* seg_chunks) {
+    const int64_t nch = (L + kQ - 1) / kQ, units = batch * H;
+    const int64_t resident = kCUs * (N > 128 ? 2 : 3);
+    int64_t n = resident / units;
+    if (n > nch / kMinSegChunks) n = nch / kMinSegChunks;
+    if (n < 2) n = 1;
+    const int64_t per = (nch + n - 1) / n;
+    *n_seg = (nch + per - 1) / per;
+    *seg_chunks = per;
+}
+
+int64_t ssd_seg_state_offset(int64_t batch, int64_t L) { return ssd_gram_bytes(batch, L); }
+
+int64_t ssd_seg_decay_offset(int64_t batch, int64_t L, int64_t H, int64_t N, int64_t n_seg) {
+    return ssd_gram_bytes(batch, L) + batch * H * (n_seg - 1) * kP * N * 4;
+}
+
+int64_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t N) {
+    int64_t n_seg, per;
+    ssd_segments(batch, L, H, N, &n_seg, &per);
+    if (n_seg == 1) return ssd_gram_bytes(batch, L);
+    return ssd_seg_decay_offset(batch, L, H, N, n_seg) + batch * H * (n_seg - 1) * 4;
+}
+
 template <int N>
 static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
     dim3 g0(static_cast<unsigned>(a.batch * ((a.L + kQ - 1) / kQ)));
     s6_timing_mark("ssd_gram", stream, true);
     hipLaunchKernelGGL((ssd_gram<N>), g0, dim3(kThreads), 0, stream, a);
     s6_timing_mark("ssd_gram", stream, false);
-    dim3 grid(static_cast<unsigned>(a.batch * a.H));
+    if (a.n_seg > 1) {
+        dim3 g1(static_cast<unsigned>(a.batch * (a.n_seg - 1) * a.H));
+        s6_timing_mark("ssd_seg_local", stream, true);
+        hipLaunchKernelGGL((ssd_chunked<N, false, true>), g1, dim3(kThreads), 0, stream, a);
+        s6_timing_mark("ssd_seg_local", stream, false);
+        dim3 g2(static_cast<unsigned>(a.batch * a.H));
+        s6_timing_mark("ssd_seg_fold", stream, true);
+        hipLaunchKernelGGL((ssd_seg_fold<N>), g2, dim3(kThreads), 0, stream, a);
+        s6_timing_mark("ssd_seg_fold", stream, false);
+    }
+    dim3 grid(static_cast<unsigned>(a.batch * a.n_seg * a.H));
     s6_timing_mark("ssd_chunked", stream, true);
-    if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((ssd_chunked<N, false>), grid, dim3(kThreads), 0, stream, a);
+    if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true, false>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((ssd_chunked<N, false, false>), grid, dim3(kThreads), 0, stream, a);
     s6_timing_mark("ssd_chunked", stream, false);
     return hipGetLastError();
 }

@@ -500,7 +500,16 @@ int64_t ssm_ssd_fwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t
     const int rc = ssd_check(batch, L, H, P, N, io_dtype);
     if (rc) return rc;
     ok();
-    return ssd_gram_bytes(batch, L);
+    return ssd_workspace_bytes(batch, L, H, N);
+}
+
+int ssm_ssd_fwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int io_dtype, int64_t* n_segments,
+                     int64_t* segment_chunks) {
+    const int rc = ssd_check(batch, L, H, P, N, io_dtype);
+    if (rc) return rc;
+    if (!n_segments || !segment_chunks) return fail(SSM_ERR_NULL, "n_segments or segment_chunks is NULL");
+    ssd_segments(batch, L, H, N, n_segments, segment_chunks);
+    return ok();
 }
 
 int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, const void* C,
@@ -519,7 +528,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
         {x, 16, "x"}, {z, 16, "z"}, {y, 16, "y"}, {delta, 2, "delta"}, {B, 16, "B"}, {C, 16, "C"},
         {A, 4, "A"}, {Dskip, 4, "Dskip"}, {dt_bias, 4, "dt_bias"}, {h0, 16, "h0"}, {h_last, 16, "h_last"},
         {workspace, 16, "workspace"}};
-    const int64_t wsb = ssd_gram_bytes(batch, L);
+    const int64_t wsb = ssd_workspace_bytes(batch, L, H, N);
     if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)wsb);
     if (workspace_bytes < wsb)
         return fail(SSM_ERR_WORKSPACE, "workspace has %lld bytes; %lld needed", (long long)workspace_bytes,
@@ -543,6 +552,12 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
         if (overlap(wr, o)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", o.name);
     SsdArgs a{};
     a.gram = static_cast<uint16_t*>(workspace);
+    ssd_segments(batch, L, H, N, &a.n_seg, &a.seg_chunks);
+    if (a.n_seg > 1) {
+        char* wsc = static_cast<char*>(workspace);
+        a.seg_state = reinterpret_cast<float*>(wsc + ssd_seg_state_offset(batch, L));
+        a.seg_decay = reinterpret_cast<float*>(wsc + ssd_seg_decay_offset(batch, L, H, N, a.n_seg));
+    }
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias;
     a.h0 = h0; a.y = y; a.h_last = h_last;
     a.batch = batch; a.L = L; a.H = H; a.N = N;

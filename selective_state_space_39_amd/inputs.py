@@ -277,7 +277,9 @@ SSD_WORKLOAD = dict(name="mamba2-2.7b-layer", batch=8, L=2048, H=80, P=64, N=128
 SSD_WORKLOADS = {w["name"]: w for w in (
     SSD_WORKLOAD,
     dict(SSD_WORKLOAD, name="mamba2-2.7b-layer-n64", N=64, seed=(SEED_ROOT, 10)),
-    dict(SSD_WORKLOAD, name="mamba2-2.7b-layer-n256", N=256, seed=(SEED_ROOT, 11)))}
+    dict(SSD_WORKLOAD, name="mamba2-2.7b-layer-n256", N=256, seed=(SEED_ROOT, 11)),
+    # one long sequence: too few (batch row, head) sequences to fill the GPU, so they are cut into segments
+    dict(SSD_WORKLOAD, name="mamba2-long-context-128k", batch=1, L=131072, seed=(SEED_ROOT, 12)))}
 
 
 def make_ssd_inputs(batch: int, L: int, H: int, P: int = 64, N: int = 128, io: str = "bf16",

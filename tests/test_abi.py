@@ -404,7 +404,10 @@ def test_host_queries_never_misbehave():
         if ws < 0:
             assert ws in errors and L.ssm_last_error()
         else:
-            assert N in (64, 128, 256) and dtype == 1 and ws == batch * -(-length // 64) * 64 * 64 * 2
+            assert N in (64, 128, 256) and dtype == 1
+            ns, sc = binding.ssd_plan(batch, length, D, N)
+            gram = batch * -(-length // 64) * 64 * 64 * 2
+            assert ws == gram + (batch * D * (ns - 1) * (64 * N + 1) * 4 if ns > 1 else 0)
 
     run()
 
@@ -436,3 +439,29 @@ def test_plans_of_plausible_shapes_are_consistent():
                 assert (ws == 0) == (nc == 1)
 
     run()
+
+
+def test_ssd_segment_plan():
+    """Sequences that fill the GPU are walked whole; fewer are cut into segments of whole 64-token chunks, at
+    least 16 chunks each except the last, covering L exactly, with every (sequence, segment) workgroup
+    resident at once (three per CU up to N = 128, two at N = 256)."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=300, deadline=None)
+    @given(batch=st.integers(1, 16), length=st.integers(1, 400000), H=st.integers(1, 128),
+           N=st.sampled_from([64, 128, 256]))
+    def run(batch, length, H, N):
+        from hypothesis import assume
+        assume(length * H * 64 * 2 <= (1 << 31) - 1)           # one batch row within 32-bit offsets
+        ns, sc = binding.ssd_plan(batch, length, H, N)
+        nch = -(-length // 64)
+        resident = 256 * (2 if N > 128 else 3)                    # workgroups resident on 256 CUs
+        assert ns >= 1 and sc >= 1 and (ns - 1) * sc < nch <= ns * sc
+        if 2 * batch * H > resident or nch < 32:
+            assert ns == 1
+        if ns > 1:
+            assert sc >= 16 and batch * H * ns <= resident
+    run()
+    assert binding.ssd_plan(8, 2048, 80, 128) == (1, 32)           # the 2.7B layer: walked whole
+    assert binding.ssd_plan(1, 131072, 80, 128) == (9, 228)        # long context, one row: 720 workgroups
+    assert binding.ssd_plan(1, 131072, 80, 256) == (6, 342)        # N = 256: two workgroups per CU

@@ -27,6 +27,23 @@ def test_ssd_matches_oracle(batch, L, H, N, gated, h0):
     assert_close(host64(h), rh, TOL["bf16"], f"ssd {batch}x{L}x{H} N={N} h_L")
 
 
+@pytest.mark.parametrize("batch,L,H,N,gated,h0,n_seg", [
+    (1, 5000, 2, 128, True, True, 4),      # 79 chunks in segments of 20, the last 19, ragged last chunk
+    (1, 3000, 3, 64, False, False, 2),     # segments of 24 and 23 chunks, no gate, zero start
+    (1, 4100, 1, 256, True, True, 4),      # N = 256, last segment 14 chunks, a 4-token last chunk
+    (2, 3000, 2, 128, True, True, 2),      # two batch rows
+])
+def test_ssd_segmented_matches_oracle(batch, L, H, N, gated, h0, n_seg):
+    """Few sequences: each is cut into segments walked in parallel (first pass, fold, layer per segment)."""
+    assert binding.ssd_plan(batch, L, H, N)[0] == n_seg
+    s = inputs.make_ssd_inputs(batch, L, H, N=N, seed=(39, 6500 + L + N + batch), gated=gated, with_h0=h0)
+    log(f"segmented ssd {batch}x{L}x{H} N {N}: plan {binding.ssd_plan(batch, L, H, N)}")
+    y, h = gpu_ssd(s, gated=gated, h0=h0)
+    ry, rh = oracle_ssd(s, gated=gated, h0=h0)
+    assert_close(host64(y), ry, TOL["bf16"], "segmented ssd y")
+    assert_close(host64(h), rh, TOL["bf16"], "segmented ssd h_L")
+
+
 def test_ssd_split_resume():
     s = inputs.make_ssd_inputs(2, 500, 3, seed=(39, 6100), with_h0=True)
     y, h = gpu_ssd(s)
