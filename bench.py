@@ -146,7 +146,8 @@ def record_traffic(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_
         t = {}
     rec = {}
     for kname in ("s6_chunk_out", "s6_chunk_carry", "s6_carry_scan", "s6_step", "s6_bwd_carries",
-                  "s6_carry_scan2", "s6_chunk_bwd", "s6_bwd_reduce", "ssd_gram", "ssd_chunked"):
+                  "s6_carry_scan2", "s6_chunk_bwd", "s6_bwd_reduce", "ssd_gram", "ssd_chunked", "ssd_seg_local",
+                  "ssd_seg_fold"):
         try:
             fk, wk = _pmc(fetch_csv, "FETCH_SIZE", kname), _pmc(write_csv, "WRITE_SIZE", kname)
         except SystemExit:

@@ -297,14 +297,15 @@ __device__ __forceinline__ void publish_state(Smem<N>& sm, const f32x4 (&st)[N /
             make_uint2(pack2(st[nb][0], st[nb][1]), pack2(st[nb][2], st[nb][3]));
 }
 
-// LOCAL = false: the layer itself, each workgroup walking one segment of one
-// (batch row, head) sequence from its starting state (the caller's h0 for
-// segment 0, the fold's result for the others) and writing its outputs.
-// LOCAL = true: the first pass of a segmented layer, each workgroup walking
-// segment k < n_seg - 1 from a zero state with no outputs and leaving its end
-// state and its total decay in the workspace.
+// One workgroup walks one segment of one (batch row, head) sequence.
+// LOCAL = false (kernel ssd_chunked): the layer itself, from the segment's
+// starting state (the caller's h0 for segment 0, the fold's result for the
+// others), writing its outputs.  LOCAL = true (kernel ssd_seg_local): the
+// first pass of a segmented layer, segment k < n_seg - 1 from a zero state
+// with no outputs, leaving its end state and its total decay in the
+// workspace.
 template <int N, bool GATED, bool LOCAL>
-__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdArgs a) {
+__device__ __forceinline__ void ssd_walk(const SsdArgs& a) {
     constexpr int NB = N / 16;            // 16-row blocks of the state's n
     constexpr int KS = N / 32;            // k-steps of a product over n
     __shared__ Smem<N> sm;
@@ -524,6 +525,16 @@ __global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdAr
     }
 }
 
+template <int N, bool GATED>
+__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdArgs a) {
+    ssd_walk<N, GATED, false>(a);
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_seg_local(SsdArgs a) {
+    ssd_walk<N, false, true>(a);
+}
+
 // ---------------------------------------------------------------------------
 // ssd_seg_fold: the starting state of every segment after the first, in
 // order: start(k + 1) = 2^decay(k) start(k) + local(k), start(0) = h0 (or
@@ -611,7 +622,7 @@ static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
     if (a.n_seg > 1) {
         dim3 g1(static_cast<unsigned>(a.batch * (a.n_seg - 1) * a.H));
         s6_timing_mark("ssd_seg_local", stream, true);
-        hipLaunchKernelGGL((ssd_chunked<N, false, true>), g1, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((ssd_seg_local<N>), g1, dim3(kThreads), 0, stream, a);
         s6_timing_mark("ssd_seg_local", stream, false);
         dim3 g2(static_cast<unsigned>(a.batch * a.H));
         s6_timing_mark("ssd_seg_fold", stream, true);
@@ -620,8 +631,8 @@ static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
     }
     dim3 grid(static_cast<unsigned>(a.batch * a.n_seg * a.H));
     s6_timing_mark("ssd_chunked", stream, true);
-    if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true, false>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((ssd_chunked<N, false, false>), grid, dim3(kThreads), 0, stream, a);
+    if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((ssd_chunked<N, false>), grid, dim3(kThreads), 0, stream, a);
     s6_timing_mark("ssd_chunked", stream, false);
     return hipGetLastError();
 }
