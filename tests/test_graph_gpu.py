@@ -65,10 +65,12 @@ def test_graph_scan_and_ssd_replays_follow_new_inputs():
     p = {k: f32dev(getattr(s, k)) for k in ("A", "Dskip", "dt_bias", "h0")}
     ws = torch.empty(binding.workspace_bytes(2, 300, 200, 1, 64), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(t["x"])
-    q = inputs.make_ssd_inputs(2, 200, 3, seed=(39, 7101), with_h0=True)
+    # an SSD shape cut into segments: the first pass, the fold and the layer are all captured
+    assert binding.ssd_plan(1, 3000, 2, 128) == (2, 24)
+    q = inputs.make_ssd_inputs(1, 3000, 2, seed=(39, 7101), with_h0=True)
     u = {k: dev(getattr(q, k), "bf16") for k in ("x", "delta", "z", "B", "C")}
     v = {k: f32dev(getattr(q, k)) for k in ("A", "Dskip", "dt_bias", "h0")}
-    wss = torch.empty(binding.ssd_workspace_bytes(2, 200, 3, 128), dtype=torch.uint8, device="cuda")
+    wss = torch.empty(binding.ssd_workspace_bytes(1, 3000, 2, 128), dtype=torch.uint8, device="cuda")
     ys = torch.empty_like(u["x"])
 
     res = {}
