@@ -66,7 +66,7 @@ typedef enum {
     SSM_ERR_DTYPE = -4,      /* unknown io dtype */
     SSM_ERR_ALIGN = -5,      /* a pointer is not aligned as required below */
     SSM_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than the query returns */
-    SSM_ERR_ALIAS = -7,      /* an output overlaps an input or another output */
+    SSM_ERR_ALIAS = -7,      /* an output overlaps an input or another output, or the workspace overlaps any argument */
     SSM_ERR_HIP = -8         /* a HIP call or kernel launch failed */
 } ssm_status;
 
@@ -117,7 +117,9 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dty
  *                   aligned; may be NULL when that size is 0.
  * Alignment: io tensors to their element size; B and C to 16 bytes; float32
  * tensors to 4 bytes.  y and h_last must not overlap any input, each other or
- * the workspace.
+ * the workspace; the workspace must not overlap any input either (the carry
+ * pass writes it while other workgroups still read the inputs).  Any such
+ * overlap is SSM_ERR_ALIAS.
  */
 int ssm_scan_fwd(const void* x, const void* delta, const void* z,
                  const void* B, const void* C,
@@ -245,7 +247,8 @@ int ssm_scan_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int io_dty
  *   workspace       at least ssm_scan_bwd_workspace_bytes(...) bytes,
  *                   256-byte aligned, required.
  * Alignment as for ssm_scan_fwd (dout, dx, ddelta, dz like x).  No output may
- * overlap an input, another output or the workspace.  The sums over channels,
+ * overlap an input, another output or the workspace, and the workspace may
+ * not overlap an input (SSM_ERR_ALIAS).  The sums over channels,
  * tokens and batch rows are taken in a fixed order: results are bitwise
  * reproducible for a given shape and chunk_len.
  */
@@ -320,6 +323,11 @@ int ssm_ssd_fwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, 
 
 /*
  * Per-kernel timing, for measurement tools; not needed to compute anything.
+ *
+ * The switch is PROCESS-WIDE state (the only mutable state of the library
+ * besides each thread's error text): while it is on, launches from every
+ * thread record events, so turn it on only in a measurement run, not in a
+ * library shared with other work.  Not for use inside graph capture.
  *
  * ssm_timing_enable(1, kernel) makes every later launch of the named kernel
  * of this library (every kernel when kernel is NULL), on any thread,

@@ -69,6 +69,23 @@ Range rng(const char* name, const void* p, int64_t bytes) {
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Outputs may overlap neither an input nor each other; the workspace may
+// overlap neither an input nor an output.  Inputs may share memory (they are
+// only read).  Returns SSM_OK or SSM_ERR_ALIAS with the pair named.
+int check_disjoint(const Range* ins, size_t nin, const Range* outs, size_t nout, const Range& ws) {
+    for (size_t o = 0; o < nout; ++o) {
+        for (size_t i = 0; i < nin; ++i)
+            if (overlap(outs[o], ins[i])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[o].name, ins[i].name);
+        for (size_t j = 0; j < o; ++j)
+            if (overlap(outs[o], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[o].name, outs[j].name);
+    }
+    for (size_t i = 0; i < nin; ++i)
+        if (overlap(ws, ins[i])) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", ins[i].name);
+    for (size_t o = 0; o < nout; ++o)
+        if (overlap(ws, outs[o])) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", outs[o].name);
+    return SSM_OK;
+}
+
 struct Plan {
     int64_t chunk_len;
     int64_t n_chunks;
@@ -414,16 +431,14 @@ int scan_fwd_impl(const void* x, const void* delta, const void* z, const void* B
     const Range ins[] = {rng("x", x, seq), rng("delta", delta, seq), rng("z", z, seq), rng("B", B, bc),
                          rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
                          rng("dt_bias", dt_bias, D * 4), rng("h0", h0, st),
-                         rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes),
                          rng("conv_w", cv.w, D * cv.k * 4), rng("conv_b", cv.b, cv.k ? D * 4 : 0),
                          rng("conv_init", cv.init, win)};
     const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st), rng("conv_last", cv.last, win)};
-    for (auto& o : outs)
-        for (auto& i : ins)
-            if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
-    for (int i = 0; i < 3; ++i)
-        for (int j = 0; j < i; ++j)
-            if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    // The carry pass writes the workspace while other workgroups still read
+    // the inputs, so it may share memory with nothing else.
+    const Range wsr = rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes);
+    if (int rc2 = check_disjoint(ins, sizeof ins / sizeof ins[0], outs, sizeof outs / sizeof outs[0], wsr))
+        return rc2;
 
     S6ScanArgs a{};
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
@@ -541,15 +556,8 @@ int ssm_ssd_fwd(const void* x, const void* delta, const void* z, const void* B, 
                          rng("B", B, bc), rng("C", C, bc), rng("A", A, H * 4), rng("Dskip", Dskip, H * 4),
                          rng("dt_bias", dt_bias, H * 4), rng("h0", h0, st)};
     const Range outs[] = {rng("y", y, seq), rng("h_last", h_last, st)};
-    for (auto& o : outs)
-        for (auto& i : ins)
-            if (overlap(o, i)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", o.name, i.name);
-    if (overlap(outs[0], outs[1])) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
-    const Range wr = rng("workspace", workspace, wsb);
-    for (auto& i : ins)
-        if (overlap(wr, i)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", i.name);
-    for (auto& o : outs)
-        if (overlap(wr, o)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", o.name);
+    if (int rc2 = check_disjoint(ins, sizeof ins / sizeof ins[0], outs, 2, rng("workspace", workspace, wsb)))
+        return rc2;
     SsdArgs a{};
     a.gram = static_cast<uint16_t*>(workspace);
     ssd_segments(batch, L, H, N, &a.n_seg, &a.seg_chunks);
@@ -631,16 +639,13 @@ int ssm_scan_bwd(const void* x, const void* delta, const void* z, const void* B,
     const Range ins[] = {rng("x", x, seq), rng("delta", delta, seq), rng("z", z, seq), rng("B", B, bc),
                          rng("C", C, bc), rng("A", A, D * kN * 4), rng("Dskip", Dskip, D * 4),
                          rng("dt_bias", dt_bias, D * 4), rng("h0", h0, st), rng("dout", dout, seq),
-                         rng("dh_last", dh_last, st), rng("workspace", workspace, p.ws_bytes)};
+                         rng("dh_last", dh_last, st)};
     const Range outs[] = {rng("dx", dx, seq), rng("ddelta", ddelta, seq), rng("dz", dz, seq),
                           rng("dB", dB, bcf), rng("dC", dC, bcf), rng("dA", dA, D * kN * 4),
                           rng("dDskip", dDskip, D * 4), rng("ddt_bias", ddt_bias, D * 4), rng("dh0", dh0, st)};
-    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
-        for (auto& in : ins)
-            if (overlap(outs[i], in)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, in.name);
-        for (size_t j = 0; j < i; ++j)
-            if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
-    }
+    const Range wsr = rng("workspace", workspace, p.ws_bytes);
+    if (int rc2 = check_disjoint(ins, sizeof ins / sizeof ins[0], outs, sizeof outs / sizeof outs[0], wsr))
+        return rc2;
 
     S6BwdArgs a{};
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.dout = dout;

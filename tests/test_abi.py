@@ -207,6 +207,22 @@ def test_bwd_plan_and_workspace():
     assert L.ssm_scan_bwd_workspace_bytes(1, 10, 8, 8, 1, 0) == E_N
 
 
+@pytest.mark.parametrize("inp", ["x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0"])
+def test_workspace_on_an_input(inp):
+    """The carry pass writes the workspace while other workgroups still read the inputs."""
+    f = Fake()
+    assert f.call(ws=f.p[inp]) == E_ALIAS
+    assert "workspace overlaps " + inp in binding.lib().ssm_last_error().decode()
+    # a workspace that starts inside the input and runs past its end overlaps it too
+    assert f.call(ws=f.p[inp] + (f.sizes[inp] - 16) // 16 * 16) == E_ALIAS
+
+
+def test_workspace_overlap_needs_a_workspace():
+    """A one-chunk plan needs no workspace: an unused pointer on top of an input is not an error."""
+    f = Fake(L=32)
+    assert f.call(chunk_len=32, ws=f.p["x"], ws_bytes=0) not in (E_ALIAS, E_WS)
+
+
 BWD_ARGS = ["x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "dout", "dh_last",
             "dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"]
 
@@ -264,6 +280,19 @@ def test_bwd_alias(out, inp):
     assert f.call(**{out: f.p[inp]}) == E_ALIAS
 
 
+@pytest.mark.parametrize("inp", ["x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "dout", "dh_last"])
+def test_bwd_workspace_on_an_input(inp):
+    f = FakeBwd()
+    assert f.call(ws=f.p[inp] // 256 * 256) == E_ALIAS
+    assert "workspace overlaps " + inp in binding.lib().ssm_last_error().decode()
+
+
+@pytest.mark.parametrize("out", ["dx", "ddelta", "dz", "dB", "dA", "dh0"])
+def test_bwd_workspace_on_an_output(out):
+    f = FakeBwd()
+    assert f.call(ws=f.p[out] // 256 * 256) == E_ALIAS
+
+
 def test_conv_scan_validation():
     f = Fake()
     v = ctypes.c_void_p
@@ -282,6 +311,12 @@ def test_conv_scan_validation():
     assert call(conv_init=v(base + (2 << 24) + 1)) == E_ALIGN
     assert call(conv_last=v(p["x"])) == E_ALIAS             # conv_last on top of xin
     assert call(conv_last=v(p["y"] + 64)) == E_ALIAS        # conv_last inside y
+    # the workspace on top of the convolution's own inputs
+    for q in (w, b, init):
+        assert L.ssm_conv_scan_fwd(v(p["x"]), w, b, 4, init, v(p["delta"]), v(p["z"]), v(p["B"]), v(p["C"]),
+                                   v(p["A"]), v(p["Dskip"]), v(p["dt_bias"]), v(p["h0"]), v(p["y"]),
+                                   v(p["h_last"]), last, f.batch, f.L, f.D, 16, f.io, 32, q, 1 << 20,
+                                   None) == E_ALIAS
 
 
 def test_conv_decode_validation():
