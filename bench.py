@@ -1,35 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 selective scan (S6) forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba-130m-layer]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long-context-128k]
 
 A step is one ssm_scan_fwd call over the whole workload (every stage of the
 hot path: step size, discretisation, chunk carries, carry fold, rescan with
 readout, gate, store), inputs already resident in HBM.  Prints one JSON line.
 
-Timing: W untimed warm-up steps, then K steps bracketed by synchronisations
-and HIP events on the stream the library launches on: that region gives
-ms_per_step and value.  Events recorded between kernels slow a step down
-(each one is a barrier on the queue), so the dominant kernel's own duration
-is taken over another K steps in which the library brackets only that kernel
-with events on its stream (ssm_timing_enable); the roofline uses that
-average.  A third pass brackets every kernel for the per-kernel breakdown.
+Default workload: long-context-128k (batch 1, 131072 tokens, 2048 channels,
+N = 16, bf16 io, fp32 state), the largest of the scan configurations that
+fit one GPU, and the one that exercises the chunk carries and their combine.
 
-Roofline.  On MI355X this path is bound by vector-ALU issue, not HBM: every
-element needs 16 exponentials and ~64 fp32 multiply/FMA operations for 8 bytes
-of HBM traffic.  The work unit is an fp32 VALU issue slot of one lane at the
-full rate: gfx950 issues a wave64 fp32 add/mul/FMA whose operands are all
-VGPRs every 2 cycles per SIMD (32 lanes per cycle; measured), which is the
-published fp32 vector peak without packed math: 256 CUs x 4 SIMDs x 32 lanes
-x 2 flops x 2.4 GHz = 157.3 TFLOP/s.  Transcendentals (exp, log, rcp) run at
-a quarter of that rate and count as four slots (an operand read from an SGPR
-halves an instruction's rate; that is the kernel's cost, not the method's).
-Reported as FMA-equivalent flops (2 per slot).  The algorithmic work per
-(b, t, d) element is 152 slots = 304 flops:
+Timing: the GPU's clocks ramp up over the first tens of milliseconds of
+load, so the step is first run untimed until 250 ms have passed (reported
+as clock_settle), then W untimed warm-up steps, then K steps bracketed by
+synchronisations and HIP events on the stream the library launches on: that
+region gives ms_per_step and value.  Events recorded between kernels slow a
+step down (each one is a barrier on the queue), so the dominant kernel's own
+duration is taken over another K steps in which the library brackets only
+that kernel with events on its stream (ssm_timing_enable); the roofline uses
+that average.  A third pass brackets every kernel for the per-kernel
+breakdown.
+
+Roofline.  The bound the pages name for this layer is HBM bandwidth, so
+`roofline` holds the dominant kernel (s6_chunk_out, one full pass of the
+method over every element per launch) against 8 TB/s: achieved = the
+workload's algorithmic bytes (x, delta, z read and y written once, B and C
+read once, parameters read, h_L written) / that kernel's average duration.
+On MI355X the kernel is in fact limited by vector-ALU issue: every element
+needs 16 exponentials and ~64 fp32 multiply/FMA operations for 8 bytes.
+`valu` reports that separately, in issue slots (not flops): a full-rate slot
+is one lane of a wave64 fp32 add/mul/FMA with VGPR operands, which gfx950
+issues every 2 cycles per SIMD (32 lanes per cycle and SIMD; measured), so
+256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6e12 slots/s.  Transcendentals
+(exp, log, rcp) count as four slots.  The method's work per (b, t, d)
+element is 152 slots:
   16 states x (mul for Delta*A, exp = 4, mul for Delta*x*B, fma for h, fma for y) = 128
   softplus (exp 4 + log 4 + 3) = 11, Delta*x 1, skip 1, silu gate (exp 4 + rcp 4 + 3) = 11.
-The achieved HBM rate (algorithmic bytes / step time) and its fraction of
-8 TB/s are reported next to it.
+(an operand read from an SGPR halves an instruction's issue rate; that is
+the kernel's cost, not the method's, and is not counted).
+
+dtype is the arithmetic type of the path (fp32 state and arithmetic);
+config.io is the storage type of x, delta, z, B, C and y.
 """
 from __future__ import annotations
 
@@ -46,6 +58,10 @@ sys.path.insert(0, ROOT)
 METRIC = "selective-scan elements/s (B·L·D) and achieved HBM GB/s vs peak, 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
 PEAK_VALU_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12    # 157.3, fp32 vector (VGPR operands, no packed math)
+PEAK_VALU_SLOTS = 256 * 4 * 32 * 2.4e9                 # 78.6e12 full-rate fp32 lane issue slots per second
+DEFAULT_WORKLOAD = "long-context-128k"
+SETTLE_MS = 250.0                   # untimed load before the warm-up steps, for the clocks to ramp up
+CPU_POOL_MAX = 16                   # worker processes of the pooled CPU baseline (the host's CPU share)
 SLOTS_PER_ELEMENT = 152
 DOMINANT = "s6_chunk_out"          # the output pass: one full pass of the method per launch
 # bench workload -> (what is timed, the named input workload it runs on)
@@ -191,26 +207,67 @@ def flushed_timing(step, stream, algorithmic_bytes, elements, reps=30):
             "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
-def cpu_baseline(s, min_seconds=10.0, max_passes=12):
-    """The float64 oracle as it stands, on the host, over whole passes of the workload."""
-    import numpy as np
+_POOL_WORK = {}
+
+
+def _pool_strip(i):
+    """One channel strip of the scan workload set up in _POOL_WORK (inherited through fork)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = None
+    s, cs = _POOL_WORK["s"], _POOL_WORK["cs"]
+    g = slice(cs * i, cs * (i + 1))
+    oracle.scan_fwd(s.x[..., g], s.delta[..., g], s.A[g], s.B, s.C, s.Dskip[g], s.dt_bias[g], z=s.z[..., g], io=s.io)
+    return os.getpid()
+
+
+def cpu_baseline_strips(s, cs=128, min_seconds=10.0):
+    """The float64 oracle as it stands, on the host, over channel strips of the workload (every token).
+
+    single core: strips run one after another until min_seconds have passed;
+    pool: every strip of the workload at once over a pool of forked worker processes
+    (min(host CPUs, 16) of them), i.e. the whole workload, timed wall-clock.
+    Must run before the process touches the GPU (the workers are forked from it)."""
+    import multiprocessing as mp
     b, L, D, _ = s.shape
-    passes, elapsed = 0, 0.0
-    while passes < max_passes and (passes == 0 or elapsed < min_seconds):
+    strips = max(1, D // cs)
+    _POOL_WORK.update(s=s, cs=cs)
+    calls, elapsed = 0, 0.0
+    while calls < strips and (calls == 0 or elapsed < min_seconds):
         t0 = time.perf_counter()
-        oracle.scan_fwd(s.x, s.delta, s.A, s.B, s.C, s.Dskip, s.dt_bias, z=s.z, io=s.io)
+        _pool_strip(calls)
         elapsed += time.perf_counter() - t0
-        passes += 1
-    value = passes * b * L * D / elapsed
-    return {"value": value, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the workload ({b}x{L}x{D}), {elapsed:.1f} s; "
-                      f"NumPy float64 elementwise loop, single-threaded (BLAS pool {blas_threads} unused)"}
+        calls += 1
+    single = calls * b * L * cs / elapsed
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host = os.cpu_count() or 1
+    workers = max(1, min(host, CPU_POOL_MAX, strips))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        pids = pool.map(_pool_strip, range(strips), chunksize=1)
+        wall = time.perf_counter() - t0
+    _POOL_WORK.clear()
+    pooled = strips * b * L * cs / wall
+    return {"value": round(pooled, 1), "unit": "elements/s", "cores": len(set(pids)), "kind": "oracle",
+            "sample": f"the whole workload as {strips} strips of {cs} channels ({b}x{L}x{cs}, every token) over a "
+                      f"pool of {workers} forked processes, {wall:.1f} s wall; NumPy float64, one thread per process "
+                      f"(host shows {host} CPUs)",
+            "single_core": {"value": round(single, 1), "unit": "elements/s", "cores": 1,
+                            "sample": f"{calls} strip(s) of {cs} channels one after another, {elapsed:.1f} s"}}
+
+
+def settle(step, min_ms=SETTLE_MS):
+    """Run the step untimed until min_ms of wall time have passed (the clocks ramp up under load)."""
+    import torch
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+    return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
 
 
 def cpu_sampled(call, elements_per_call, what, min_seconds=10.0, max_calls=400):
@@ -268,6 +325,7 @@ def bench_decode(args):
         else:
             binding.state_update(h, x, dl, tA, B, C, tD, tb, z=z, out=y)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream(dev)
@@ -294,6 +352,7 @@ def bench_decode(args):
     out = {"metric": METRIC, "value": round(batch * D / (ms_per_step * 1e-3), 1), "unit": "elements/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "clock_settle": settled,
            "config": {"workload": f"{args.workload} {'ssm_conv_state_update' if conv else 'ssm_state_update'}",
                       "batch": batch, "D": D, "N": 16, "io": "bf16", "state": "f32", "gated": True,
                       **({"conv_k": CONV_K} if conv else {})},
@@ -356,6 +415,7 @@ def bench_bwd(args, name):
     def step():
         binding.scan_bwd(x, dl, A, B, C, Dk, bias, dout, z=z, chunk_len=args.chunk_len, workspace=ws, grads=grads)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream(dev)
@@ -392,7 +452,7 @@ def bench_bwd(args, name):
     out = {"metric": "selective-scan backward elements/s (B·L·D), 1 MI355X", "value": round(E / (ms_per_step * 1e-3), 1),
            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32", "data": "synthetic",
+           "dtype": "f32", "data": "synthetic", "clock_settle": settled,
            "config": {"workload": f"{args.workload} ssm_scan_bwd", "batch": batch, "L": L, "D": D, "N": N, "io": io,
                       "state": "f32", "gated": True, "chunk_len": chunk_len, "n_chunks": n_chunks},
            "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
@@ -453,6 +513,7 @@ def bench_ssd(args, name):
     def step():
         binding.ssd_fwd(x, dl, A, B, C, Dk, bias, z=z, out=y, return_last_state=False, workspace=ws)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream(dev)
@@ -486,7 +547,7 @@ def bench_ssd(args, name):
     out = {"metric": "SSD layer elements/s (B·L·H·P), 1 MI355X", "value": round(E / (ms_per_step * 1e-3), 1),
            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16", "data": "synthetic",
+           "dtype": "bf16", "data": "synthetic", "clock_settle": settled,
            "config": {"workload": f"{name} ssm_ssd_fwd", "batch": batch, "L": L, "H": H, "P": P, "N": N,
                       "io": "bf16", "state": "f32", "gated": True, "chunk": 64,
                       "segments": binding.ssd_plan(batch, L, H, N, P)[0]},
@@ -515,11 +576,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The GPU's clocks take tens of milliseconds of load to settle: 300 untimed
-    # steps (50 ms for the 130M-layer scan) put the timed steps in steady state;
-    # after 5 the step time still reads ~10 % high.
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="mamba-130m-layer", choices=sorted(WORKLOADS))
+    # The clocks are settled by SETTLE_MS of untimed load before the warm-up
+    # steps (settle()), so a few warm-up steps suffice.
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--chunk-len", type=int, default=0)
     ap.add_argument("--heads", type=int, default=0,
                     help="SSD workloads: run the layer with this many heads instead (an occupancy sweep; the "
@@ -544,20 +604,28 @@ def main():
               "run N independent copies).", file=sys.stderr)
         sys.exit(2)
 
+    kind, name = WORKLOADS[args.workload]
+    conv = args.workload.endswith("-conv")
+    from selective_state_space_39_amd import inputs
+    s = cpu = None
+    if kind == "scan":
+        s = inputs.make_workload(name)
+        # the pooled oracle forks worker processes: before anything touches the GPU
+        if not args.no_cpu_baseline and not conv:
+            cpu = cpu_baseline_strips(s)
+
     import torch
-    from selective_state_space_39_amd import binding, inputs
+    from selective_state_space_39_amd import binding
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    kind, name = WORKLOADS[args.workload]
     if kind == "ssd":
         return bench_ssd(args, name)
     if kind == "decode":
         return bench_decode(args)
     if kind == "bwd":
         return bench_bwd(args, name)
-    s = inputs.make_workload(name)
     batch, L, D, N = s.shape
     io = s.io
     dev = torch.device("cuda:0")
@@ -576,7 +644,6 @@ def main():
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     chunk_len, n_chunks = binding.plan(batch, L, D, io_code, args.chunk_len)
 
-    conv = args.workload.endswith("-conv")
     if conv:
         cp = inputs.make_conv_params(batch, D, CONV_K, io=io, seed=inputs.SCAN_WORKLOADS[name]["seed"])
         cw, cb = f32(cp.w), f32(cp.b)
@@ -588,6 +655,7 @@ def main():
         def step():
             binding.scan_fwd(x, dl, A, B, C, Dk, bias, z=z, chunk_len=args.chunk_len, out=y, workspace=ws)
 
+    settled = settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -623,20 +691,28 @@ def main():
     E = batch * L * D
     value = E / (ms_per_step * 1e-3)
     abytes = algorithmic_bytes(batch, L, D, N, 2 if io == "bf16" else 4)
+    if conv:                                        # conv taps and bias read, conv_last not requested
+        abytes += D * (CONV_K + 1) * 4
     hbm_gbps = abytes / (ms_per_step * 1e-3) / 1e9
 
     dominant = DOMINANT
     launches, kms = kern[dominant]
     avg_ms = kms / launches
+    achieved = abytes / (avg_ms * 1e-3) / 1e9       # one launch = one full pass over every element
     slots = SLOTS_PER_ELEMENT + (CONV_SLOTS if conv else 0)
-    work_flops = E * slots * 2                      # one full pass of the method per launch
-    achieved = work_flops / (avg_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload, dominant)
-    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_VALU_TFLOPS, 2),
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_VALU_TFLOPS, 4), "traffic": traffic,
+    slot_rate = E * slots / (avg_ms * 1e-3)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(args.workload, dominant),
                 "kernel": dominant, "avg_launch_ms": round(avg_ms, 5),
-                "work": f"{slots} full-rate fp32 VALU slots (= {2 * slots} FMA-equivalent flops) "
-                        f"per element x {E} elements per launch" + (" (incl. the width-4 convolution)" if conv else "")}
+                "work": f"{abytes} algorithmic bytes per launch = {abytes / E:.4f} B per element x {E} elements "
+                        f"(x, delta, z read and y written once, B and C read, parameters read, h_L written); "
+                        f"one launch is one full pass of the method"}
+    valu = {"unit": "full-rate fp32 VALU lane issue slots per second", "slots_per_element": slots,
+            "achieved": round(slot_rate / 1e12, 3), "peak": round(PEAK_VALU_SLOTS / 1e12, 3), "scale": 1e12,
+            "frac": round(slot_rate / PEAK_VALU_SLOTS, 4), "kernel": dominant,
+            "note": "the method's issue slots per element (exp, log, rcp = 4 slots) over the dominant kernel's "
+                    "duration: the limit this kernel actually meets on gfx950" + (
+                        " (incl. the width-4 convolution)" if conv else "")}
     kernels = {n: {"launches": c, "avg_ms": round(t / c, 5)} for n, (c, t) in breakdown.items()}
     kernels["_note"] = (f"every kernel bracketed by events in a separate pass: {ms_all:.4f} ms per step "
                         f"with the events, {ms_per_step:.4f} without")
@@ -648,12 +724,14 @@ def main():
            "config": {"workload": f"{args.workload} {'ssm_conv_scan_fwd' if conv else 'ssm_scan_fwd'}",
                       "batch": batch, "L": L, "D": D, "N": N, "io": io, "state": "f32", "gated": True,
                       "chunk_len": chunk_len, "n_chunks": n_chunks, **({"conv_k": CONV_K} if conv else {})},
+           "clock_settle": settled,
            "hbm": {"achieved_gbps": round(hbm_gbps, 1), "peak_gbps": PEAK_HBM_GBPS,
-                   "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes},
-           "roofline": roofline, "kernels": kernels,
+                   "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": abytes,
+                   "note": "whole step (every kernel of the call) against 8 TB/s"},
+           "roofline": roofline, "valu": valu, "kernels": kernels,
            "mall_flushed": None if args.no_flushed else flushed_timing(step, stream, abytes, E)}
-    if not args.no_cpu_baseline and not conv:
-        out["cpu_baseline"] = cpu_baseline(s)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     elif not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_sampled(
