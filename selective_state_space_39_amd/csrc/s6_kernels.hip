@@ -158,76 +158,146 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// phase 2: combine the chunk carries in order
+// phase 2: combine the chunk carries (reduce, then scan, then re-fold)
 // ---------------------------------------------------------------------------
-// One wavefront per (batch row, 64 channels, state n): lanes are channels, so
-// every carry read and every prefix write is one coalesced 256-byte row.  The
-// carries of up to kScanBlk chunks are loaded at once, then combined in
-// order: h <- exp(A_n S_c) h + H_c, starting from `init` (zero when NULL).
-// The combined prefix after carry c overwrites H_c.  The forward scan folds
-// carries in chunk order from h0 (prefix c = starting state of chunk c+1);
-// the backward pass folds its adjoint carries in reverse order from dh_last
-// (the same combine: the adjoint obeys the transposed recurrence).
-constexpr int kScanBlk = 16;
+// One workgroup of W wavefronts per (batch row, 64 channels, state n); lanes
+// are channels, so every carry read and every prefix write is a coalesced
+// 256-byte row.  The combine of two carries, (S1,H1) then (S2,H2) =
+// (S1+S2, e2 H1 + H2) with e = exp(A_n S), is associative ("Mamba", "Scan
+// View"), so the ncar carries are scanned in three steps per round of up to
+// W x kFoldSeg carries:
+//   1. wavefront w loads a contiguous segment of carries into registers (all
+//      loads in flight at once), turns each S into e, and folds the segment
+//      from zero into its aggregate (E = product of e, H);
+//   2. the W aggregates of each channel are transposed through LDS so that a
+//      channel's segments sit in W consecutive lanes, and scanned with
+//      log2(W) DPP row shifts (Hillis-Steele, the left operand first), giving
+//      each segment's exclusive prefix and so its starting state from the
+//      round's incoming state;
+//   3. every wavefront re-folds its segment from that starting state (the e
+//      are still in registers) and writes each prefix over its H in place.
+// A carry is read once and written once.  The prefix after carry c is the
+// true starting state of chunk c+1.  The forward folds the carries in chunk
+// order from h0; the backward folds its adjoint carries in reverse order
+// from dh_last (the same combine: the adjoint obeys the transposed recurrence).
+constexpr int kFoldSeg = 32;          // carries per wavefront and round
+constexpr int kFoldMaxW = 16;         // wavefronts per workgroup (a DPP row is 16 lanes)
 
-__device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t bid) {
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+// value of lane (l - s) in the same 16-lane row; lanes with l % 16 < s keep `self`
+__device__ __forceinline__ float row_shr(float self, float v, int s) {
+    const int iv = __float_as_int(v), is = __float_as_int(self);
+    int r;
+    switch (s) {
+        case 1: r = __builtin_amdgcn_update_dpp(is, iv, 0x111, 0xf, 0xf, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(is, iv, 0x112, 0xf, 0xf, false); break;
+        case 4: r = __builtin_amdgcn_update_dpp(is, iv, 0x114, 0xf, 0xf, false); break;
+        default: r = __builtin_amdgcn_update_dpp(is, iv, 0x118, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+
+struct FoldLds {
+    float e[kFoldMaxW][kWave + 1];      // segment aggregates (padded rows: the transposed reads hit distinct banks)
+    float h[kFoldMaxW][kWave + 1];
+    float start[kFoldMaxW][kWave + 1];  // starting state of every segment
+    float pre[kWave];                   // incoming state of the round, per channel
+};
+
+// W: wavefronts in the workgroup (1, 2, 4, 8 or 16; blockDim.x = 64 W).
+__device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t unit, int W, FoldLds& sm) {
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int l = threadIdx.x & (kWave - 1);
     const int64_t gx = (a.D + kWave - 1) / kWave;               // 64-channel groups per batch row
-    const int64_t unit = bid * (kBlock / kWave) + wave;
-    if (unit >= a.batch * gx * kN) return;                      // whole wavefront past the end
     const int n = static_cast<int>(unit % kN);
     const int64_t grp = unit / kN;
     const int64_t b = grp / gx;
     const int64_t first = (grp % gx) * kWave;
-    const int64_t dl = first + (threadIdx.x & (kWave - 1));
-    const int64_t d = dl < a.D ? dl : a.D - 1;
+    const int64_t dl = first + l;
+    const bool active = dl < a.D;
+    const int64_t d = active ? dl : a.D - 1;
     const int64_t ncar = a.ncar;
     const float A2 = a.A[d * kN + n] * kLog2e;
-    float h = a.init ? a.init[(b * a.D + d) * kN + n] : 0.0f;
     const float* S = a.S + b * ncar * a.D + d;
     float* H = a.H + (b * ncar * kN + n) * a.D + d;
     const int64_t hs = kN * a.D;                                // H stride between carries
-    // Blocks of kScanBlk carries, double-buffered: the next block's loads are
-    // issued before this block's prefix stores (written in that order, so the
-    // compiler, which cannot prove they touch other addresses, keeps it), and
-    // a block costs one memory round trip only at the start.
-    auto load_blk = [&](int64_t k0, float (&Sv)[kScanBlk], float (&Hv)[kScanBlk]) {
+    if (w == 0) sm.pre[l] = a.init ? a.init[(b * a.D + d) * kN + n] : 0.0f;
+    // the transposed view of step 2: this thread scans segment sg of channel ch
+    const int ch = static_cast<int>(threadIdx.x) / W, sg = static_cast<int>(threadIdx.x) % W;
+
+    for (int64_t base = 0; base < ncar; base += static_cast<int64_t>(W) * kFoldSeg) {
+        const int64_t rem = min(ncar - base, static_cast<int64_t>(W) * kFoldSeg);
+        const int seg = static_cast<int>((rem + W - 1) / W);
+        const int64_t k0 = base + static_cast<int64_t>(w) * seg;
+        const int cnt = static_cast<int>(max(min(rem - static_cast<int64_t>(w) * seg, static_cast<int64_t>(seg)),
+                                             static_cast<int64_t>(0)));
+        // 1. load the segment, fold it from zero
+        float e[kFoldSeg], hv[kFoldSeg];
 #pragma unroll
-        for (int k = 0; k < kScanBlk; ++k) {
-            const int64_t kk = k0 + k < ncar ? k0 + k : ncar - 1;
-            const int64_t c = a.reverse ? ncar - 1 - kk : kk;
-            Sv[k] = S[c * a.D];
-            Hv[k] = H[c * hs];
-        }
-    };
-    auto fold_blk = [&](int64_t k0, const float (&Sv)[kScanBlk], const float (&Hv)[kScanBlk]) {
-#pragma unroll
-        for (int k = 0; k < kScanBlk; ++k) {
-            if (k0 + k < ncar) {                                  // wave-uniform
-                const int64_t c = a.reverse ? ncar - 1 - (k0 + k) : k0 + k;
-                h = fmaf(__builtin_amdgcn_exp2f(A2 * Sv[k]), h, Hv[k]);
-                H[c * hs] = h;
+        for (int k = 0; k < kFoldSeg; ++k) {
+            if (k < cnt) {                                          // wave-uniform
+                const int64_t kk = k0 + k;
+                const int64_t c = a.reverse ? ncar - 1 - kk : kk;
+                e[k] = S[c * a.D];
+                hv[k] = H[c * hs];
             }
         }
-    };
-    float S0[kScanBlk], H0[kScanBlk], S1[kScanBlk], H1[kScanBlk];
-    load_blk(0, S0, H0);
-    for (int64_t k0 = 0; k0 < ncar; k0 += 2 * kScanBlk) {
-        if (k0 + kScanBlk < ncar) load_blk(k0 + kScanBlk, S1, H1);
-        fold_blk(k0, S0, H0);
-        if (k0 + kScanBlk >= ncar) break;
-        if (k0 + 2 * kScanBlk < ncar) load_blk(k0 + 2 * kScanBlk, S0, H0);
-        fold_blk(k0 + kScanBlk, S1, H1);
+        float ae = 1.0f, ah = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kFoldSeg; ++k) {
+            if (k < cnt) {
+                e[k] = __builtin_amdgcn_exp2f(A2 * e[k]);
+                ah = fmaf(e[k], ah, hv[k]);
+                ae *= e[k];
+            }
+        }
+        sm.e[w][l] = ae;
+        sm.h[w][l] = ah;
+        __syncthreads();
+        // 2. scan the W segment aggregates of each channel across lanes
+        {
+            float se = sm.e[sg][ch], sh = sm.h[sg][ch];
+            for (int s = 1; s < W; s <<= 1) {
+                const float pe = row_shr(se, se, s), ph = row_shr(sh, sh, s);
+                if (sg >= s) {                                      // (pe, ph) then (se, sh)
+                    sh = fmaf(se, ph, sh);
+                    se *= pe;
+                }
+            }
+            float xe = row_shr(1.0f, se, 1), xh = row_shr(0.0f, sh, 1);
+            if (sg == 0) { xe = 1.0f; xh = 0.0f; }
+            const float p = sm.pre[ch];
+            sm.start[sg][ch] = fmaf(xe, p, xh);
+            __syncthreads();                                        // every thread has read pre
+            if (sg == W - 1) sm.pre[ch] = fmaf(se, p, sh);          // incoming state of the next round
+        }
+        __syncthreads();
+        // 3. re-fold the segment from its starting state, prefixes over H
+        float h = sm.start[w][l];
+#pragma unroll
+        for (int k = 0; k < kFoldSeg; ++k) {
+            if (k < cnt) {
+                h = fmaf(e[k], h, hv[k]);
+                const int64_t kk = k0 + k;
+                const int64_t c = a.reverse ? ncar - 1 - kk : kk;
+                if (active) H[c * hs] = h;
+            }
+        }
+        __syncthreads();                                            // LDS is reused by the next round
     }
 }
 
-__global__ __launch_bounds__(kBlock) void s6_carry_scan(S6FoldArgs a) { fold_body(a, blockIdx.x); }
+__global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan(S6FoldArgs a, int W) {
+    __shared__ FoldLds sm;
+    fold_body(a, blockIdx.x, W, sm);
+}
 
 // two independent folds (the backward's state and adjoint carries) in one launch
-__global__ __launch_bounds__(kBlock) void s6_carry_scan2(S6FoldArgs a, S6FoldArgs b, int64_t first) {
+__global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan2(S6FoldArgs a, S6FoldArgs b, int64_t first,
+                                                                   int W) {
+    __shared__ FoldLds sm;
     const int64_t i = blockIdx.x;
-    if (i < first) fold_body(a, i);
-    else fold_body(b, i - first);
+    if (i < first) fold_body(a, i, W, sm);
+    else fold_body(b, i - first, W, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -477,19 +547,27 @@ static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Wavefronts per fold workgroup: enough that each holds ~8 carries or more per round, at most 16.
+static int fold_waves(int64_t ncar) {
+    int W = 1;
+    while (W < kFoldMaxW && static_cast<int64_t>(W) * 8 < ncar) W *= 2;
+    return W;
+}
+
 void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
-    const int64_t waves = f.batch * ((f.D + kWave - 1) / kWave) * kN;
-    dim3 g(static_cast<unsigned>((waves + kBlock / kWave - 1) / (kBlock / kWave)));
+    const int64_t units = f.batch * ((f.D + kWave - 1) / kWave) * kN;
+    const int W = fold_waves(f.ncar);
     s6_timing_mark(name, stream, true);
-    hipLaunchKernelGGL(s6_carry_scan, g, dim3(kBlock), 0, stream, f);
+    hipLaunchKernelGGL(s6_carry_scan, dim3(static_cast<unsigned>(units)), dim3(kWave * W), 0, stream, f, W);
     s6_timing_mark(name, stream, false);
 }
 
 void s6_launch_fold2(const S6FoldArgs& f0, const S6FoldArgs& f1, const char* name, hipStream_t stream) {
-    const int64_t waves = f0.batch * ((f0.D + kWave - 1) / kWave) * kN;
-    const int64_t per = (waves + kBlock / kWave - 1) / (kBlock / kWave);
+    const int64_t units = f0.batch * ((f0.D + kWave - 1) / kWave) * kN;
+    const int W = fold_waves(f0.ncar);
     s6_timing_mark(name, stream, true);
-    hipLaunchKernelGGL(s6_carry_scan2, dim3(static_cast<unsigned>(2 * per)), dim3(kBlock), 0, stream, f0, f1, per);
+    hipLaunchKernelGGL(s6_carry_scan2, dim3(static_cast<unsigned>(2 * units)), dim3(kWave * W), 0, stream, f0, f1,
+                       units, W);
     s6_timing_mark(name, stream, false);
 }
 
