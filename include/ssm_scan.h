@@ -131,6 +131,37 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z,
                  void* stream);
 
 /*
+ * ssm_scan_fwd for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation while running.
+ * The same computation and kernels as ssm_scan_fwd, with no workspace
+ * argument: the chunk carries go to a fixed scratch array inside the library
+ * (64 MiB, 2^26 bytes, one copy per GPU, held until the process ends), and
+ * the call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  The first call on a device looks up that device's address of
+ * the array once.
+ *
+ *   Arguments, layout, alignment and errors as ssm_scan_fwd.
+ *   chunk_len       0 = the library's plan among the chunk lengths whose
+ *                   carries, batch * (chunks - 1) * D * (N + 1) * 4 bytes,
+ *                   fit the scratch (SSM_ERR_WORKSPACE if none does); an
+ *                   explicit chunk_len whose carries do not fit is
+ *                   SSM_ERR_WORKSPACE.  With the same chunk_len the results are
+ *                   bit-identical to ssm_scan_fwd's.
+ * Every call on one GPU shares that GPU's scratch: calls that can overlap in
+ * time on one GPU (on different streams, or from different threads without
+ * ordering between their streams) race and give wrong results.  Order them
+ * on one stream.  Nothing in the scratch needs to start at any value; it
+ * holds the last call's carries afterwards.
+ */
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const void* z,
+                         const void* B, const void* C,
+                         const float* A, const float* Dskip, const float* dt_bias,
+                         const float* h0,
+                         void* y, float* h_last,
+                         int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                         int64_t chunk_len, void* stream);
+
+/*
  * The scan fed by the block's local convolution, fused: the scan input is
  *
  *     x_t = silu(conv_b_d + sum_{k<K} conv_w_dk * xin_{t-K+1+k})

@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_plan.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.ssm_scan_fwd.restype = i32
     L.ssm_scan_fwd.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
+    L.ssm_scan_fwd_noalloc.restype = i32
+    L.ssm_scan_fwd_noalloc.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp]
     L.ssm_conv_scan_fwd.restype = i32
     L.ssm_conv_scan_fwd.argtypes = [vp, vp, vp, i64, vp] + [vp] * 11 + [i64, i64, i64, i64, i32, i64, vp, i64, vp]
     L.ssm_conv_state_update.restype = i32
@@ -164,6 +166,42 @@ def scan_fwd(x, delta, A, B, C, D, dt_bias, z=None, h0=None, chunk_len: int = 0,
     rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
                             _ptr(h0), _ptr(y), _ptr(h_last), batch, L, Dc, N_STATE, io, chunk_len,
                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return y, h_last
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D, dt_bias, z=None, h0=None, chunk_len: int = 0, out=None,
+                     h_last_out=None, return_last_state: bool = True):
+    """scan_fwd through ssm_scan_fwd_noalloc: no workspace, the chunk carries
+    go to the library's fixed per-GPU scratch.  Pass `out` (and `h_last_out`)
+    to allocate nothing here either.  Returns (y, h_last)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, D)")
+    batch, L, Dc = x.shape
+    dev = x.device
+    io = _io(x)
+    dt = x.dtype
+    _need(x, "x", (batch, L, Dc), dt, dev)
+    _need(delta, "delta", (batch, L, Dc), dt, dev)
+    if z is not None:
+        _need(z, "z", (batch, L, Dc), dt, dev)
+    _need(B, "B", (batch, L, N_STATE), dt, dev)
+    _need(C, "C", (batch, L, N_STATE), dt, dev)
+    _need(A, "A", (Dc, N_STATE), torch.float32, dev)
+    _need(D, "D", (Dc,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (Dc,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, Dc, N_STATE), torch.float32, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", (batch, L, Dc), dt, dev)
+    h_last = None
+    if return_last_state:
+        h_last = (torch.empty((batch, Dc, N_STATE), dtype=torch.float32, device=dev) if h_last_out is None
+                  else h_last_out)
+        _need(h_last, "h_last_out", (batch, Dc, N_STATE), torch.float32, dev)
+    rc = lib().ssm_scan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+                                    _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last), batch, L, Dc, N_STATE, io,
+                                    chunk_len, _stream(dev))
     _check(rc)
     return y, h_last
 

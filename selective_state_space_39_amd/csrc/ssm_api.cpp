@@ -161,17 +161,37 @@ int check_chunk_len(int64_t D, int64_t chunk_len) {
     return SSM_OK;
 }
 
-int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
+// Forward workspace for n chunks: carry_S (batch, n-1, D) then carry_H
+// (batch, n-1, N, D), float32, 256-byte aligned parts; -1 on overflow.
+int64_t fwd_ws_bytes(int64_t batch, int64_t n_chunks, int64_t D) {
+    if (n_chunks <= 1) return 0;
+    const int64_t carries = mul_ck(mul_ck(batch, n_chunks - 1), D);
+    if (carries < 0 || mul_ck(carries, kN * 4) < 0) return -1;
+    return (carries * 4 + 255) / 256 * 256 + carries * kN * 4;
+}
+
+// max_ws >= 0: only plans whose workspace fits max_ws bytes (the automatic
+// plan searches among those; an explicit chunk_len beyond it is an error).
+int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p, int64_t max_ws = -1) {
     if (int rc = check_chunk_len(D, chunk_len)) return rc;
+    auto fits = [&](int64_t len) {
+        const int64_t w = fwd_ws_bytes(batch, (L + len - 1) / len, D);
+        return max_ws < 0 || (w >= 0 && w <= max_ws);
+    };
     if (chunk_len == 0) {
         const int64_t whole = std::min((L + kChunkAlign - 1) / kChunkAlign * kChunkAlign, max_chunk_len(D));
         int64_t best = whole;
         double best_t = est_plan(batch, D, L, whole);
+        bool found = fits(whole);
         for (int64_t len = whole - kChunkAlign; len >= kMinChunk; len -= kChunkAlign) {
             if ((L + len - 1) / len > kMaxGrid) break;
+            if (!fits(len)) continue;
             const double t = est_plan(batch, D, L, len);
-            if (t < best_t * 0.999) { best_t = t; best = len; }
+            if (!found || t < best_t * 0.999) { best_t = t; best = len; found = true; }
         }
+        if (!found)
+            return fail(SSM_ERR_WORKSPACE, "no chunk plan of this shape keeps its carries within %lld bytes of scratch",
+                        (long long)max_ws);
         chunk_len = best;
     }
     p.chunk_len = chunk_len;
@@ -182,11 +202,11 @@ int make_plan(int64_t batch, int64_t L, int64_t D, int64_t chunk_len, Plan& p) {
     // one workgroup per (256-channel block, batch row, chunk) in a 1-D grid
     if (batch * ((D + 255) / 256) * p.n_chunks > (int64_t(1) << 31) - 1)
         return fail(SSM_ERR_SHAPE, "batch * ceil(D / 256) * chunks exceeds the grid limit");
-    const int64_t carries = mul_ck(mul_ck(batch, p.n_chunks - 1), D);
-    if (carries < 0) return fail(SSM_ERR_SHAPE, "workspace size overflows");
-    // carry_S (batch, n-1, D) then carry_H (batch, n-1, N, D), float32, 256-byte aligned parts
-    const int64_t sb = (carries * 4 + 255) / 256 * 256;
-    p.ws_bytes = (p.n_chunks > 1) ? sb + carries * kN * 4 : 0;
+    p.ws_bytes = fwd_ws_bytes(batch, p.n_chunks, D);
+    if (p.ws_bytes < 0) return fail(SSM_ERR_SHAPE, "workspace size overflows");
+    if (max_ws >= 0 && p.ws_bytes > max_ws)
+        return fail(SSM_ERR_WORKSPACE, "chunk_len = %lld needs %lld bytes of carries; the scratch holds %lld",
+                    (long long)p.chunk_len, (long long)p.ws_bytes, (long long)max_ws);
     return SSM_OK;
 }
 
@@ -387,16 +407,58 @@ struct ConvArgs {
     void* last = nullptr;
 };
 
+// ---------------------------------------------------------------------------
+// scratch of the no-allocation entry point
+// ---------------------------------------------------------------------------
+// The chunk carries of ssm_scan_fwd_noalloc live in this fixed array instead
+// of a caller workspace.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever passed to a kernel.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_dev;          // device address of `scratch`, per device ordinal
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device; SSM_ERR_HIP if the runtime cannot give it.
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(SSM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (static_cast<size_t>(dev) >= g_scratch_dev.size()) g_scratch_dev.resize(dev + 1, nullptr);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return SSM_OK;
+}
+
+// use_scratch: the carries go to the library's scratch array (the workspace
+// arguments are ignored) and the plan is restricted to carries that fit it.
 int scan_fwd_impl(const void* x, const void* delta, const void* z, const void* B, const void* C,
                   const float* A, const float* Dskip, const float* dt_bias, const float* h0,
                   void* y, float* h_last, const ConvArgs& cv,
                   int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
-                  int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
+                  int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream,
+                  bool use_scratch = false) {
     int rc = check_shape(batch, L, D, N, io_dtype);
     if (rc) return rc;
     Plan p;
-    rc = make_plan(batch, L, D, chunk_len, p);
+    rc = make_plan(batch, L, D, chunk_len, p, use_scratch ? kScratchBytes : -1);
     if (rc) return rc;
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
 
     struct { const void* p; const char* n; } req[] = {
         {x, cv.k ? "xin" : "x"}, {delta, "delta"}, {B, "B"}, {C, "C"}, {A, "A"}, {Dskip, "Dskip"},
@@ -409,7 +471,7 @@ int scan_fwd_impl(const void* x, const void* delta, const void* z, const void* B
         if (!cv.w) return fail(SSM_ERR_NULL, "conv_w is NULL");
         if (!cv.b) return fail(SSM_ERR_NULL, "conv_b is NULL");
     }
-    if (p.ws_bytes > 0) {
+    if (p.ws_bytes > 0 && !use_scratch) {
         if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL; %lld bytes needed", (long long)p.ws_bytes);
         if (workspace_bytes < p.ws_bytes)
             return fail(SSM_ERR_WORKSPACE, "workspace has %lld bytes; %lld needed",
@@ -439,6 +501,9 @@ int scan_fwd_impl(const void* x, const void* delta, const void* z, const void* B
     const Range wsr = rng("workspace", p.ws_bytes ? workspace : nullptr, p.ws_bytes);
     if (int rc2 = check_disjoint(ins, sizeof ins / sizeof ins[0], outs, sizeof outs / sizeof outs[0], wsr))
         return rc2;
+    if (use_scratch && p.ws_bytes > 0) {
+        if (int rc2 = scratch_on_current_device(&workspace)) return rc2;
+    }
 
     S6ScanArgs a{};
     a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
@@ -471,6 +536,15 @@ int ssm_scan_fwd(const void* x, const void* delta, const void* z, const void* B,
                  int64_t chunk_len, void* workspace, int64_t workspace_bytes, void* stream) {
     return scan_fwd_impl(x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last, ConvArgs{}, batch, L, D, N,
                          io_dtype, chunk_len, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const void* z, const void* B, const void* C,
+                         const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                         void* y, float* h_last,
+                         int64_t batch, int64_t L, int64_t D, int64_t N, int io_dtype,
+                         int64_t chunk_len, void* stream) {
+    return scan_fwd_impl(x, delta, z, B, C, A, Dskip, dt_bias, h0, y, h_last, ConvArgs{}, batch, L, D, N,
+                         io_dtype, chunk_len, nullptr, 0, stream, true);
 }
 
 int ssm_conv_scan_fwd(const void* xin, const float* conv_w, const float* conv_b, int64_t conv_k,

@@ -223,6 +223,34 @@ def test_workspace_overlap_needs_a_workspace():
     assert f.call(chunk_len=32, ws=f.p["x"], ws_bytes=0) not in (E_ALIAS, E_WS)
 
 
+def _noalloc(f, chunk_len=32, **over):
+    p = dict(f.p)
+    p.update(over)
+    v = lambda k: ctypes.c_void_p(p[k]) if p[k] is not None else None
+    return binding.lib().ssm_scan_fwd_noalloc(v("x"), v("delta"), v("z"), v("B"), v("C"), v("A"), v("Dskip"),
+                                              v("dt_bias"), v("h0"), v("y"), v("h_last"), f.batch, f.L, f.D, 16,
+                                              f.io, chunk_len, None)
+
+
+def test_noalloc_validation():
+    """ssm_scan_fwd_noalloc validates like ssm_scan_fwd, and refuses plans whose carries exceed its scratch."""
+    f = Fake()
+    assert _noalloc(f, x=None) == E_NULL
+    assert _noalloc(f, y=f.p["x"]) == E_ALIAS
+    assert _noalloc(f, B=f.p["B"] + 8) == E_ALIGN
+    assert _noalloc(f, chunk_len=40) == E_SHAPE
+    # 2 x 64 x 128 in 32-token chunks needs a few KB: valid, so only the missing device stops it here
+    assert _noalloc(f) == -8
+    # 1 x 65536 x 2048 in 64-token chunks: 1023 chunk carries of 2048 channels x 17 floats = 142 MB > 64 MiB
+    assert _noalloc(Fake(1, 65536, 2048), chunk_len=64) == E_WS
+    assert "scratch" in binding.lib().ssm_last_error().decode()
+    # the automatic plan picks chunks whose carries fit (the workspace plan of this shape needs 68 MiB)
+    assert binding.workspace_bytes(1, 131072, 2048, 1, 0) > 64 << 20
+    assert _noalloc(Fake(1, 131072, 2048), chunk_len=0) == -8
+    # no plan fits: 2^20 channels cap a chunk at 480 tokens, and 2184 carries of 2^20 channels are far too many
+    assert _noalloc(Fake(1, 1 << 20, 1 << 20), chunk_len=0) == E_WS
+
+
 BWD_ARGS = ["x", "delta", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "dout", "dh_last",
             "dx", "ddelta", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"]
 
