@@ -58,6 +58,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// v rounded to the nearest bf16 value (ties to even), as a float; finite v
+__device__ __forceinline__ float round_bf16(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -287,6 +292,46 @@ __device__ __forceinline__ void stage_chunk(Smem<N>& sm, const StageRegs<N>& r, 
     }
 }
 
+// State update of this wavefront's channels, state^T = dec state^T + B^T (W x)
+// with W_i = exp(S_end - S_i) Delta_i.  W x is formed in fp32 and enters the
+// matrix cores as two bf16 operands, its rounded value and the rounding
+// remainder (x and B are bf16 inputs, exact as operands), so the carried fp32
+// state sees W x to ~2^-17 rather than bf16's 2^-9: the state handed to a
+// decode step or a following segment keeps fp32-level accuracy.
+template <int N>
+__device__ __forceinline__ void state_update(const Smem<N>& sm, f32x4 (&st)[N / 16], float dec, int w) {
+    const int l = threadIdx.x & 63, q = l >> 4;
+    bf16x8 xh[2], xl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int i0 = 32 * ks + 8 * q;
+        const bf16x8 xv = opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, i0, 16 * w);
+        const float4 wa = *reinterpret_cast<const float4*>(&sm.Wt[i0]);
+        const float4 wb = *reinterpret_cast<const float4*>(&sm.Wt[i0 + 4]);
+        const float wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        float v[8], hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[j] = static_cast<float>(xv[j]) * wi[j];
+            hv[j] = round_bf16(v[j]);
+            v[j] -= hv[j];
+        }
+        xh[ks] = pack8(hv);                // exact: hv holds bf16 values
+        xl[ks] = pack8(v);
+    }
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) {
+        const bf16x8 b0 = opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16);
+        const bf16x8 b1 = opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16);
+        f32x4 sv = st[nb] * dec;
+        sv = mfma(b0, xl[0], sv);
+        sv = mfma(b1, xl[1], sv);
+        sv = mfma(b0, xh[0], sv);
+        sv = mfma(b1, xh[1], sv);
+        st[nb] = sv;
+    }
+}
+
 // bf16 copy of this wavefront's state channels into St[p][n]
 template <int N>
 __device__ __forceinline__ void publish_state(Smem<N>& sm, const f32x4 (&st)[N / 16], int w) {
@@ -385,27 +430,7 @@ __device__ __forceinline__ void ssd_walk(const SsdArgs& a) {
             // state update only: state^T = exp(S_end) state^T + B^T (W x)
             const float s_end = sm.S2[kQ - 1];
             decay += s_end;
-            const float dec = __builtin_amdgcn_exp2f(s_end);
-            bf16x8 xw[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int i0 = 32 * ks + 8 * q;
-                const bf16x8 xv = opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, i0, 16 * w);
-                const float4 wa = *reinterpret_cast<const float4*>(&sm.Wt[i0]);
-                const float4 wb = *reinterpret_cast<const float4*>(&sm.Wt[i0 + 4]);
-                const float wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-                float v[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(xv[j]) * wi[j];
-                xw[ks] = pack8(v);
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f32x4 sv = st[nb] * dec;
-                sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw[0], sv);
-                sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw[1], sv);
-                st[nb] = sv;
-            }
+            state_update<N>(sm, st, __builtin_amdgcn_exp2f(s_end), w);
             __syncthreads();                           // every read of Xs, Bs of this chunk is done
             continue;
         }
@@ -455,30 +480,10 @@ __device__ __forceinline__ void ssd_walk(const SsdArgs& a) {
         load_cg<N>(io, cn, t1, w, own);
 
         // --- state update: state^T = exp(S_end) state^T + B^T (W x), W_i = exp(S_end - S_i) Delta_i
-        const float dec = __builtin_amdgcn_exp2f(sm.S2[kQ - 1]);
-        bf16x8 xw[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int i0 = 32 * ks + 8 * q;
-            const bf16x8 xv = opnd_rows8(&sm.Xs[0][0], Smem<N>::kLdX, i0, 16 * w);
-            const float4 wa = *reinterpret_cast<const float4*>(&sm.Wt[i0]);
-            const float4 wb = *reinterpret_cast<const float4*>(&sm.Wt[i0 + 4]);
-            const float wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(xv[j]) * wi[j];
-            xw[ks] = pack8(v);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            f32x4 sv = st[nb] * dec;
-            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 8 * q, nb * 16), xw[0], sv);
-            sv = mfma(opnd_rows8(&sm.Bs[0][0], Smem<N>::kLdB, 32 + 8 * q, nb * 16), xw[1], sv);
-            st[nb] = sv;
-        }
+        state_update<N>(sm, st, __builtin_amdgcn_exp2f(sm.S2[kQ - 1]), w);
         __syncthreads();                               // every read of St, Xs, Bs of this chunk is done
 
-        // --- outputs in row order through this wavefront's staging rows, gate, store
+        // --- outputs in row order through this wavefront's staging rows, gate (when z is given), store
         float* ysm = ystage<N>(sm, w);
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
@@ -490,7 +495,7 @@ __device__ __forceinline__ void ssd_walk(const SsdArgs& a) {
             const float4 u0 = *reinterpret_cast<const float4*>(src);
             const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
             float yv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-            if constexpr (GATED) {
+            if (GATED && a.z) {                      // uniform: one kernel serves both (z NULL: its loads read 0)
                 const uint32_t zw[4] = {own.z[k].x, own.z[k].y, own.z[k].z, own.z[k].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -525,13 +530,18 @@ __device__ __forceinline__ void ssd_walk(const SsdArgs& a) {
     }
 }
 
+// Occupancy is pinned (three workgroups per CU up to N = 128, two at 256), so
+// the compiler schedules for the register budget the layout needs instead of
+// chasing a higher occupancy it cannot keep.
 template <int N, bool GATED>
-__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_chunked(SsdArgs a) {
+__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) __attribute__((amdgpu_waves_per_eu(N > 128 ? 2 : 3, N > 128 ? 2 : 3)))
+void ssd_chunked(SsdArgs a) {
     ssd_walk<N, GATED, false>(a);
 }
 
 template <int N>
-__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) void ssd_seg_local(SsdArgs a) {
+__global__ __launch_bounds__(kThreads, (N > 128 ? 2 : 3)) __attribute__((amdgpu_waves_per_eu(N > 128 ? 2 : 3, N > 128 ? 2 : 3)))
+void ssd_seg_local(SsdArgs a) {
     ssd_walk<N, false, true>(a);
 }
 
@@ -631,8 +641,9 @@ static hipError_t launch_ssd_n(const SsdArgs& a, hipStream_t stream) {
     }
     dim3 grid(static_cast<unsigned>(a.batch * a.n_seg * a.H));
     s6_timing_mark("ssd_chunked", stream, true);
-    if (a.z) hipLaunchKernelGGL((ssd_chunked<N, true>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((ssd_chunked<N, false>), grid, dim3(kThreads), 0, stream, a);
+    // one instantiation for gated and ungated layers: the gate is a uniform branch on a.z (the
+    // ungated instantiation at N = 128 does not fit its registers with the two-part state update)
+    hipLaunchKernelGGL((ssd_chunked<N, true>), grid, dim3(kThreads), 0, stream, a);
     s6_timing_mark("ssd_chunked", stream, false);
     return hipGetLastError();
 }

@@ -8,6 +8,16 @@ from selective_state_space_39_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
 
+# The carried state is fp32 and the state update's W x enters the matrix cores
+# as two bf16 parts, so up to N = 128 the final state is held to fp32-level
+# accuracy, beyond the io bound every output meets; N = 256 takes its W x as
+# one bf16 operand.
+STATE_TOL = 1e-4
+
+
+def state_bound(N):
+    return STATE_TOL if N <= 128 else TOL["bf16"]
+
 
 @pytest.mark.parametrize("batch,L,H,N,gated,h0", [
     (2, 200, 3, 128, True, True),      # 4 chunks, the last one 8 tokens
@@ -24,7 +34,7 @@ def test_ssd_matches_oracle(batch, L, H, N, gated, h0):
     y, h = gpu_ssd(s, gated=gated, h0=h0)
     ry, rh = oracle_ssd(s, gated=gated, h0=h0)
     assert_close(host64(y), ry, TOL["bf16"], f"ssd {batch}x{L}x{H} N={N} y")
-    assert_close(host64(h), rh, TOL["bf16"], f"ssd {batch}x{L}x{H} N={N} h_L")
+    assert_close(host64(h), rh, state_bound(N), f"ssd {batch}x{L}x{H} N={N} h_L")
 
 
 @pytest.mark.parametrize("batch,L,H,N,gated,h0,n_seg", [
@@ -41,7 +51,7 @@ def test_ssd_segmented_matches_oracle(batch, L, H, N, gated, h0, n_seg):
     y, h = gpu_ssd(s, gated=gated, h0=h0)
     ry, rh = oracle_ssd(s, gated=gated, h0=h0)
     assert_close(host64(y), ry, TOL["bf16"], "segmented ssd y")
-    assert_close(host64(h), rh, TOL["bf16"], "segmented ssd h_L")
+    assert_close(host64(h), rh, state_bound(N), "segmented ssd h_L")
 
 
 def test_ssd_split_resume():
@@ -79,7 +89,7 @@ def test_ssd_full_size_sampled_heads(name):
     heads = [0, 41, 79]
     ry, rh = oracle_ssd(s, heads=heads, h0=False)
     assert_close(host64(y)[:, :, heads], ry, TOL["bf16"], f"ssd {name} y (3 heads)")
-    assert_close(host64(h)[:, heads], rh, TOL["bf16"], f"ssd {name} h_L (3 heads)")
+    assert_close(host64(h)[:, heads], rh, state_bound(w["N"]), f"ssd {name} h_L (3 heads)")
 
 
 def test_ssd_errors():
