@@ -257,9 +257,11 @@ def cpu_baseline_strips(s, cs=128, min_seconds=10.0):
                             "sample": f"{calls} strip(s) of {cs} channels one after another, {elapsed:.1f} s"}}
 
 
-def settle(step, min_ms=SETTLE_MS):
+def settle(step, min_ms=None):
     """Run the step untimed until min_ms of wall time have passed (the clocks ramp up under load)."""
     import torch
+    if min_ms is None:
+        min_ms = SETTLE_MS
     torch.cuda.synchronize()
     t0, n = time.perf_counter(), 0
     while (time.perf_counter() - t0) * 1e3 < min_ms:
@@ -573,6 +575,7 @@ def bench_ssd(args, name):
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -585,6 +588,8 @@ def main():
                     help="SSD workloads: run the layer with this many heads instead (an occupancy sweep; the "
                          "line's config then names the changed shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed load before the warm-up steps (0 for counter runs under a profiler)")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the cache-flushed single steps (kernel traces then cover the timed loops only)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -592,6 +597,7 @@ def main():
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files into profiles/traffic.json")
     args = ap.parse_args()
+    SETTLE_MS = args.settle_ms
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic)
         return
