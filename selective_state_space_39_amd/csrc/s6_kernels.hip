@@ -196,31 +196,75 @@ __device__ __forceinline__ float row_shr(float self, float v, int s) {
     return __int_as_float(r);
 }
 
-struct FoldLds {
-    float e[kFoldMaxW][kWave + 1];      // segment aggregates (padded rows: the transposed reads hit distinct banks)
-    float h[kFoldMaxW][kWave + 1];
-    float start[kFoldMaxW][kWave + 1];  // starting state of every segment
-    float pre[kWave];                   // incoming state of the round, per channel
+// Unit (batch row, 64 channels, state n) of the fold: the lane's channel and
+// its carry rows.
+struct FoldUnit {
+    int64_t b, d, ncar, hs;
+    bool active;
+    float A2;
+    const float* S;
+    float* H;
+    __device__ __forceinline__ FoldUnit(const S6FoldArgs& a, int64_t unit) {
+        const int l = threadIdx.x & (kWave - 1);
+        const int64_t gx = (a.D + kWave - 1) / kWave;           // 64-channel groups per batch row
+        const int n = static_cast<int>(unit % kN);
+        const int64_t grp = unit / kN;
+        b = grp / gx;
+        const int64_t dl = (grp % gx) * kWave + l;
+        active = dl < a.D;
+        d = active ? dl : a.D - 1;
+        ncar = a.ncar;
+        A2 = a.A[d * kN + n] * kLog2e;
+        S = a.S + b * ncar * a.D + d;
+        H = a.H + (b * ncar * kN + n) * a.D + d;
+        hs = kN * a.D;                                          // H stride between carries
+    }
+    __device__ __forceinline__ int64_t slot(const S6FoldArgs& a, int64_t k) const {
+        return a.reverse ? ncar - 1 - k : k;
+    }
+    __device__ __forceinline__ float init(const S6FoldArgs& a, int64_t unit) const {
+        return a.init ? a.init[(b * a.D + d) * kN + unit % kN] : 0.0f;
+    }
 };
 
-// W: wavefronts in the workgroup (1, 2, 4, 8 or 16; blockDim.x = 64 W).
-__device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t unit, int W, FoldLds& sm) {
+// Chains of at most kFoldSeg carries: one wavefront per unit loads every carry
+// at once and folds them in order (no cross-wavefront scan, no LDS).
+__device__ __forceinline__ void fold_short(const S6FoldArgs& a, int64_t unit) {
+    const FoldUnit u(a, unit);
+    const int cnt = static_cast<int>(u.ncar);
+    float e[kFoldSeg], hv[kFoldSeg];
+#pragma unroll
+    for (int k = 0; k < kFoldSeg; ++k) {
+        if (k < cnt) {                                              // wave-uniform
+            const int64_t c = u.slot(a, k);
+            e[k] = u.S[c * a.D];
+            hv[k] = u.H[c * u.hs];
+        }
+    }
+    float h = u.init(a, unit);
+#pragma unroll
+    for (int k = 0; k < kFoldSeg; ++k) {
+        if (k < cnt) {
+            h = fmaf(__builtin_amdgcn_exp2f(u.A2 * e[k]), h, hv[k]);
+            if (u.active) u.H[u.slot(a, k) * u.hs] = h;
+        }
+    }
+}
+
+// W wavefronts per unit (blockDim.x = 64 W), LDS: segment aggregates e, h and
+// starting states, W rows of 65 floats each (padded: the transposed reads hit
+// distinct banks), and the incoming state of the round (64 floats).
+__device__ __forceinline__ void fold_scan(const S6FoldArgs& a, int64_t unit, int W, float* lds) {
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int l = threadIdx.x & (kWave - 1);
-    const int64_t gx = (a.D + kWave - 1) / kWave;               // 64-channel groups per batch row
-    const int n = static_cast<int>(unit % kN);
-    const int64_t grp = unit / kN;
-    const int64_t b = grp / gx;
-    const int64_t first = (grp % gx) * kWave;
-    const int64_t dl = first + l;
-    const bool active = dl < a.D;
-    const int64_t d = active ? dl : a.D - 1;
-    const int64_t ncar = a.ncar;
-    const float A2 = a.A[d * kN + n] * kLog2e;
-    const float* S = a.S + b * ncar * a.D + d;
-    float* H = a.H + (b * ncar * kN + n) * a.D + d;
-    const int64_t hs = kN * a.D;                                // H stride between carries
-    if (w == 0) sm.pre[l] = a.init ? a.init[(b * a.D + d) * kN + n] : 0.0f;
+    const FoldUnit u(a, unit);
+    constexpr int kRow = kWave + 1;
+    float* se = lds;
+    float* sh = se + W * kRow;
+    float* sst = sh + W * kRow;
+    float* spre = sst + W * kRow;
+    const int64_t ncar = u.ncar;
+    if (w == 0) spre[l] = u.init(a, unit);
     // the transposed view of step 2: this thread scans segment sg of channel ch
     const int ch = static_cast<int>(threadIdx.x) / W, sg = static_cast<int>(threadIdx.x) % W;
 
@@ -235,69 +279,84 @@ __device__ __forceinline__ void fold_body(const S6FoldArgs& a, int64_t unit, int
 #pragma unroll
         for (int k = 0; k < kFoldSeg; ++k) {
             if (k < cnt) {                                          // wave-uniform
-                const int64_t kk = k0 + k;
-                const int64_t c = a.reverse ? ncar - 1 - kk : kk;
-                e[k] = S[c * a.D];
-                hv[k] = H[c * hs];
+                const int64_t c = u.slot(a, k0 + k);
+                e[k] = u.S[c * a.D];
+                hv[k] = u.H[c * u.hs];
             }
         }
         float ae = 1.0f, ah = 0.0f;
 #pragma unroll
         for (int k = 0; k < kFoldSeg; ++k) {
             if (k < cnt) {
-                e[k] = __builtin_amdgcn_exp2f(A2 * e[k]);
+                e[k] = __builtin_amdgcn_exp2f(u.A2 * e[k]);
                 ah = fmaf(e[k], ah, hv[k]);
                 ae *= e[k];
             }
         }
-        sm.e[w][l] = ae;
-        sm.h[w][l] = ah;
+        se[w * kRow + l] = ae;
+        sh[w * kRow + l] = ah;
         __syncthreads();
         // 2. scan the W segment aggregates of each channel across lanes
         {
-            float se = sm.e[sg][ch], sh = sm.h[sg][ch];
+            float ve = se[sg * kRow + ch], vh = sh[sg * kRow + ch];
             for (int s = 1; s < W; s <<= 1) {
-                const float pe = row_shr(se, se, s), ph = row_shr(sh, sh, s);
-                if (sg >= s) {                                      // (pe, ph) then (se, sh)
-                    sh = fmaf(se, ph, sh);
-                    se *= pe;
+                const float pe = row_shr(ve, ve, s), ph = row_shr(vh, vh, s);
+                if (sg >= s) {                                      // (pe, ph) then (ve, vh)
+                    vh = fmaf(ve, ph, vh);
+                    ve *= pe;
                 }
             }
-            float xe = row_shr(1.0f, se, 1), xh = row_shr(0.0f, sh, 1);
+            float xe = row_shr(1.0f, ve, 1), xh = row_shr(0.0f, vh, 1);
             if (sg == 0) { xe = 1.0f; xh = 0.0f; }
-            const float p = sm.pre[ch];
-            sm.start[sg][ch] = fmaf(xe, p, xh);
-            __syncthreads();                                        // every thread has read pre
-            if (sg == W - 1) sm.pre[ch] = fmaf(se, p, sh);          // incoming state of the next round
+            const float p = spre[ch];
+            sst[sg * kRow + ch] = fmaf(xe, p, xh);
+            __syncthreads();                                        // every thread has read the incoming state
+            if (sg == W - 1) spre[ch] = fmaf(ve, p, vh);            // incoming state of the next round
         }
         __syncthreads();
         // 3. re-fold the segment from its starting state, prefixes over H
-        float h = sm.start[w][l];
+        float h = sst[w * kRow + l];
 #pragma unroll
         for (int k = 0; k < kFoldSeg; ++k) {
             if (k < cnt) {
                 h = fmaf(e[k], h, hv[k]);
-                const int64_t kk = k0 + k;
-                const int64_t c = a.reverse ? ncar - 1 - kk : kk;
-                if (active) H[c * hs] = h;
+                if (u.active) u.H[u.slot(a, k0 + k) * u.hs] = h;
             }
         }
         __syncthreads();                                            // LDS is reused by the next round
     }
 }
 
+// LDS bytes of fold_scan for W wavefronts
+static inline size_t fold_lds_bytes(int W) { return (3 * static_cast<size_t>(W) * (kWave + 1) + kWave) * sizeof(float); }
+
+// SHORT: four units per workgroup, one wavefront each (fold_short); else one
+// unit per workgroup of W wavefronts (fold_scan, dynamic LDS).
+template <bool SHORT>
 __global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan(S6FoldArgs a, int W) {
-    __shared__ FoldLds sm;
-    fold_body(a, blockIdx.x, W, sm);
+    extern __shared__ float fold_lds[];
+    if constexpr (SHORT) {
+        const int64_t unit = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + (threadIdx.x >> 6);
+        if (unit < a.batch * ((a.D + kWave - 1) / kWave) * kN) fold_short(a, unit);
+    } else {
+        fold_scan(a, blockIdx.x, W, fold_lds);
+    }
 }
 
 // two independent folds (the backward's state and adjoint carries) in one launch
+template <bool SHORT>
 __global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan2(S6FoldArgs a, S6FoldArgs b, int64_t first,
                                                                    int W) {
-    __shared__ FoldLds sm;
+    extern __shared__ float fold_lds[];
     const int64_t i = blockIdx.x;
-    if (i < first) fold_body(a, i, W, sm);
-    else fold_body(b, i - first, W, sm);
+    if constexpr (SHORT) {
+        const int64_t units = a.batch * ((a.D + kWave - 1) / kWave) * kN;
+        const int64_t unit = (i < first ? i : i - first) * (kBlock / kWave) + (threadIdx.x >> 6);
+        if (unit < units) fold_short(i < first ? a : b, unit);
+    } else {
+        if (i < first) fold_scan(a, i, W, fold_lds);
+        else fold_scan(b, i - first, W, fold_lds);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -547,10 +606,12 @@ static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Wavefronts per fold workgroup: enough that each holds ~8 carries or more per round, at most 16.
+// Wavefronts per fold unit: one while a wavefront can hold every carry in one
+// round (the short path: no cross-wavefront scan, no LDS), then as many as
+// keep each at most kFoldSeg carries per round, at most 16.
 static int fold_waves(int64_t ncar) {
     int W = 1;
-    while (W < kFoldMaxW && static_cast<int64_t>(W) * 8 < ncar) W *= 2;
+    while (W < kFoldMaxW && static_cast<int64_t>(W) * kFoldSeg < ncar) W *= 2;
     return W;
 }
 
@@ -558,7 +619,12 @@ void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
     const int64_t units = f.batch * ((f.D + kWave - 1) / kWave) * kN;
     const int W = fold_waves(f.ncar);
     s6_timing_mark(name, stream, true);
-    hipLaunchKernelGGL(s6_carry_scan, dim3(static_cast<unsigned>(units)), dim3(kWave * W), 0, stream, f, W);
+    if (W == 1)
+        hipLaunchKernelGGL(s6_carry_scan<true>, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kBlock), 0, stream,
+                           f, W);
+    else
+        hipLaunchKernelGGL(s6_carry_scan<false>, dim3(static_cast<unsigned>(units)), dim3(kWave * W),
+                           fold_lds_bytes(W), stream, f, W);
     s6_timing_mark(name, stream, false);
 }
 
@@ -566,8 +632,14 @@ void s6_launch_fold2(const S6FoldArgs& f0, const S6FoldArgs& f1, const char* nam
     const int64_t units = f0.batch * ((f0.D + kWave - 1) / kWave) * kN;
     const int W = fold_waves(f0.ncar);
     s6_timing_mark(name, stream, true);
-    hipLaunchKernelGGL(s6_carry_scan2, dim3(static_cast<unsigned>(2 * units)), dim3(kWave * W), 0, stream, f0, f1,
-                       units, W);
+    if (W == 1) {
+        const int64_t per = (units + 3) / 4;
+        hipLaunchKernelGGL(s6_carry_scan2<true>, dim3(static_cast<unsigned>(2 * per)), dim3(kBlock), 0, stream, f0, f1,
+                           per, W);
+    } else {
+        hipLaunchKernelGGL(s6_carry_scan2<false>, dim3(static_cast<unsigned>(2 * units)), dim3(kWave * W),
+                           fold_lds_bytes(W), stream, f0, f1, units, W);
+    }
     s6_timing_mark(name, stream, false);
 }
 
