@@ -614,7 +614,7 @@ def main():
     conv = args.workload.endswith("-conv")
     from selective_state_space_39_amd import inputs
     s = cpu = None
-    if kind == "scan":
+    if kind in ("scan", "conv"):
         s = inputs.make_workload(name)
         # the pooled oracle forks worker processes: before anything touches the GPU
         if not args.no_cpu_baseline and not conv:
