@@ -356,18 +356,22 @@ int ssm_ssd_fwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, 
  * Per-kernel timing, for measurement tools; not needed to compute anything.
  *
  * The switch is PROCESS-WIDE state (the only mutable state of the library
- * besides each thread's error text): while it is on, launches from every
- * thread record events, so turn it on only in a measurement run, not in a
- * library shared with other work.  Not for use inside graph capture.
+ * besides each thread's error text and the no-allocation scratch address of
+ * each device): while it is on, launches from every thread record events, so
+ * turn it on only in a measurement run, not in a library shared with other work.
+ * Not for use inside graph capture.
  *
  * ssm_timing_enable(1, kernel) makes every later launch of the named kernel
  * of this library (every kernel when kernel is NULL), on any thread,
  * bracketed by two hipEvents recorded on the launch's own stream;
- * ssm_timing_enable(0, NULL) stops recording.  Recording events between
- * kernels costs time, so time whole calls with recording off.  Kernel names:
+ * ssm_timing_enable(0, NULL) stops recording.  Each pair spans the kernel plus
+ * a few microseconds of dispatch around it, which matters only for kernels of
+ * tens of microseconds; recording events between kernels also costs time, so
+ * time whole calls with recording off.  Kernel names:
  * "s6_chunk_carry", "s6_carry_scan", "s6_chunk_out", "s6_step", and for the
  * backward "s6_bwd_carries", "s6_carry_scan2", "s6_chunk_bwd",
- * "s6_bwd_reduce", and for the SSD layer "ssd_gram", "ssd_chunked".  Returns SSM_OK.
+ * "s6_bwd_reduce", and for the SSD layer "ssd_gram", "ssd_seg_local",
+ * "ssd_seg_fold", "ssd_chunked".  Returns SSM_OK.
  *
  * ssm_timing_collect waits for every recorded event, then writes for up to
  * max_kernels distinct kernels their name (static strings owned by the
