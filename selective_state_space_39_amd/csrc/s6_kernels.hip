@@ -330,33 +330,71 @@ __device__ __forceinline__ void fold_scan(const S6FoldArgs& a, int64_t unit, int
 // LDS bytes of fold_scan for W wavefronts
 static inline size_t fold_lds_bytes(int W) { return (3 * static_cast<size_t>(W) * (kWave + 1) + kWave) * sizeof(float); }
 
-// SHORT: four units per workgroup, one wavefront each (fold_short); else one
-// unit per workgroup of W wavefronts (fold_scan, dynamic LDS).
-template <bool SHORT>
-__global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan(S6FoldArgs a, int W) {
-    extern __shared__ float fold_lds[];
-    if constexpr (SHORT) {
-        const int64_t unit = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + (threadIdx.x >> 6);
-        if (unit < a.batch * ((a.D + kWave - 1) / kWave) * kN) fold_short(a, unit);
+// Workgroup i of a fold launch -> its first unit ((batch row, 64-channel
+// group) x kN + state), or -1 past the end; `per` units per workgroup (1 or
+// 4).  Workgroups are dealt to the XCDs round-robin (i % 8).  The kN states of
+// a group read the same S rows, and a channel block's carries were written on
+// the XCD that wg_coords gave it: when the channel blocks spread evenly over
+// the XCDs, the fold of a group runs on that same XCD (which also reads its
+// prefixes next); otherwise the workgroups of a group still share one XCD.
+__device__ __forceinline__ int64_t fold_unit(int64_t i, int64_t batch, int64_t D, int per) {
+    const int64_t G = (D + kWave - 1) / kWave;                  // 64-channel groups per batch row
+    const int64_t gx = (D + kBlock - 1) / kBlock;               // channel blocks per batch row
+    const int64_t nblk = gx * batch, bpg = kN / per;            // workgroups per group
+    const int64_t x = i % kXcds, j = i / kXcds;
+    int64_t b, c;
+    if (nblk % kXcds == 0) {
+        const int64_t pb = (kBlock / kWave) * bpg;              // workgroups per channel block
+        const int64_t blk = x * (nblk / kXcds) + j / pb;
+        b = blk / gx;
+        c = (blk % gx) * (kBlock / kWave) + (j % pb) / bpg;
+        if (c >= G) return -1;
     } else {
-        fold_scan(a, blockIdx.x, W, fold_lds);
+        const int64_t grp = (j / bpg) * kXcds + x;
+        if (grp >= batch * G) return -1;
+        b = grp / G;
+        c = grp % G;
+    }
+    return (b * G + c) * kN + (j % bpg) * per;
+}
+
+// Workgroups of a fold launch (a multiple of kXcds).
+static inline int64_t fold_blocks(int64_t batch, int64_t D, int per) {
+    const int64_t G = (D + kWave - 1) / kWave, gx = (D + kBlock - 1) / kBlock, bpg = kN / per;
+    if (gx * batch % kXcds == 0) return gx * batch * (kBlock / kWave) * bpg;
+    return (batch * G + kXcds - 1) / kXcds * kXcds * bpg;
+}
+
+// SHORT: four units per workgroup, one wavefront each (fold_short); else one
+// unit per workgroup of W wavefronts (fold_scan, dynamic LDS).  A workgroup
+// with no unit leaves before any barrier.
+template <bool SHORT>
+__device__ __forceinline__ void fold_dispatch(const S6FoldArgs& a, int64_t i, int W, float* lds) {
+    if constexpr (SHORT) {
+        const int64_t u0 = fold_unit(i, a.batch, a.D, kBlock / kWave);
+        if (u0 >= 0) fold_short(a, u0 + (threadIdx.x >> 6));
+    } else {
+        const int64_t unit = fold_unit(i, a.batch, a.D, 1);
+        if (unit >= 0) fold_scan(a, unit, W, lds);
     }
 }
 
-// two independent folds (the backward's state and adjoint carries) in one launch
+template <bool SHORT>
+__global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan(S6FoldArgs a, int W) {
+    extern __shared__ float fold_lds[];
+    fold_dispatch<SHORT>(a, blockIdx.x, W, fold_lds);
+}
+
+// two independent folds (the backward's state and adjoint carries) in one
+// launch; `first` (the first fold's workgroups) is a multiple of kXcds, so
+// both keep their XCD placement
 template <bool SHORT>
 __global__ __launch_bounds__(kWave * kFoldMaxW) void s6_carry_scan2(S6FoldArgs a, S6FoldArgs b, int64_t first,
                                                                    int W) {
     extern __shared__ float fold_lds[];
     const int64_t i = blockIdx.x;
-    if constexpr (SHORT) {
-        const int64_t units = a.batch * ((a.D + kWave - 1) / kWave) * kN;
-        const int64_t unit = (i < first ? i : i - first) * (kBlock / kWave) + (threadIdx.x >> 6);
-        if (unit < units) fold_short(i < first ? a : b, unit);
-    } else {
-        if (i < first) fold_scan(a, i, W, fold_lds);
-        else fold_scan(b, i - first, W, fold_lds);
-    }
+    if (i < first) fold_dispatch<SHORT>(a, i, W, fold_lds);
+    else fold_dispatch<SHORT>(b, i - first, W, fold_lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -616,29 +654,28 @@ static int fold_waves(int64_t ncar) {
 }
 
 void s6_launch_fold(const S6FoldArgs& f, const char* name, hipStream_t stream) {
-    const int64_t units = f.batch * ((f.D + kWave - 1) / kWave) * kN;
     const int W = fold_waves(f.ncar);
     s6_timing_mark(name, stream, true);
     if (W == 1)
-        hipLaunchKernelGGL(s6_carry_scan<true>, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(kBlock), 0, stream,
-                           f, W);
+        hipLaunchKernelGGL(s6_carry_scan<true>, dim3(static_cast<unsigned>(fold_blocks(f.batch, f.D, kBlock / kWave))),
+                           dim3(kBlock), 0, stream, f, W);
     else
-        hipLaunchKernelGGL(s6_carry_scan<false>, dim3(static_cast<unsigned>(units)), dim3(kWave * W),
-                           fold_lds_bytes(W), stream, f, W);
+        hipLaunchKernelGGL(s6_carry_scan<false>, dim3(static_cast<unsigned>(fold_blocks(f.batch, f.D, 1))),
+                           dim3(kWave * W), fold_lds_bytes(W), stream, f, W);
     s6_timing_mark(name, stream, false);
 }
 
 void s6_launch_fold2(const S6FoldArgs& f0, const S6FoldArgs& f1, const char* name, hipStream_t stream) {
-    const int64_t units = f0.batch * ((f0.D + kWave - 1) / kWave) * kN;
     const int W = fold_waves(f0.ncar);
     s6_timing_mark(name, stream, true);
     if (W == 1) {
-        const int64_t per = (units + 3) / 4;
+        const int64_t per = fold_blocks(f0.batch, f0.D, kBlock / kWave);
         hipLaunchKernelGGL(s6_carry_scan2<true>, dim3(static_cast<unsigned>(2 * per)), dim3(kBlock), 0, stream, f0, f1,
                            per, W);
     } else {
-        hipLaunchKernelGGL(s6_carry_scan2<false>, dim3(static_cast<unsigned>(2 * units)), dim3(kWave * W),
-                           fold_lds_bytes(W), stream, f0, f1, units, W);
+        const int64_t per = fold_blocks(f0.batch, f0.D, 1);
+        hipLaunchKernelGGL(s6_carry_scan2<false>, dim3(static_cast<unsigned>(2 * per)), dim3(kWave * W),
+                           fold_lds_bytes(W), stream, f0, f1, per, W);
     }
     s6_timing_mark(name, stream, false);
 }

@@ -5,7 +5,9 @@ aggregates across lanes, and re-folds; a workgroup has 1, 2, 4, 8 or 16
 wavefronts (one while 32 carries or fewer, then enough for at most 32 carries
 each), and takes the carries in rounds of up to 512.  These cases put the carry count on each side of every change,
 forward (folded from h0) and backward (the adjoint folded in reverse from
-dh_last), and compare with the float64 oracle.
+dh_last), and compare with the float64 oracle.  Workgroups are placed on the
+XCD that wrote their carries when the channel blocks spread evenly over the
+XCDs: the 8 x 300-channel cases take that placement with partial groups.
 """
 import pytest
 
@@ -33,6 +35,32 @@ def test_forward_combine(ncar):
     ry, rh = oracle_scan(s, h0=s.h0)
     assert_close(host64(y), ry, TOL["f32"], f"{ncar} carries y")
     assert_close(host64(h), rh, TOL["f32"], f"{ncar} carries h_L")
+
+
+@pytest.mark.parametrize("ncar", [20, 100])
+def test_forward_combine_xcd_placed(ncar):
+    """8 batch rows of 300 channels: 16 channel blocks, a multiple of the 8
+    XCDs, so each group is combined on the XCD its carries came from; the
+    second block of a row holds one partial 64-channel group and three empty
+    ones."""
+    L = _length(ncar)
+    s = inputs.make_scan_inputs(8, L, 300, io="f32", seed=(39, 7200 + ncar), with_h0=True)
+    log(f"forward combine, 8 x 300 channels: {ncar} carries, L {L}")
+    y, h = gpu_scan(s, chunk_len=CHUNK, h0=s.h0)
+    ry, rh = oracle_scan(s, h0=s.h0)
+    assert_close(host64(y), ry, TOL["f32"], f"8 x 300, {ncar} carries y")
+    assert_close(host64(h), rh, TOL["f32"], f"8 x 300, {ncar} carries h_L")
+
+
+@pytest.mark.parametrize("ncar", [20, 100])
+def test_backward_combine_xcd_placed(ncar):
+    L = _length(ncar)
+    s = inputs.make_scan_inputs(8, L, 300, io="f32", seed=(39, 7300 + ncar), with_h0=True, A_random=True)
+    go = inputs.make_grad_outputs(8, L, 300, io="f32", seed=(39, 7300 + ncar), with_dh_last=True)
+    log(f"backward combine, 8 x 300 channels: {ncar} carries, L {L}")
+    g = gpu_bwd(s, go, chunk_len=CHUNK)
+    ref = oracle_bwd(s, go)
+    assert_grads_close(g, ref, TOL["f32"], f"bwd 8 x 300, {ncar} carries")
 
 
 @pytest.mark.parametrize("ncar", [31, 129, 513])
