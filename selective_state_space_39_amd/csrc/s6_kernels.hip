@@ -181,7 +181,12 @@ __global__ __launch_bounds__(kBlock) void s6_chunk_carry(S6ScanArgs a) {
 // order from h0; the backward folds its adjoint carries in reverse order
 // from dh_last (the same combine: the adjoint obeys the transposed recurrence).
 constexpr int kFoldSeg = 32;          // carries per wavefront and round
-constexpr int kFoldMaxW = 16;         // wavefronts per workgroup (a DPP row is 16 lanes)
+// Wavefronts per workgroup, at most 16 (a DPP row is 16 lanes).  Eight: at
+// ~114 VGPRs two such workgroups share a CU, so every unit of a 128k-token
+// combine is resident at once and takes its 511 carries in two rounds, one
+// round's stores overlapping the next one's loads (33.2 us against 35.5 with
+// sixteen wavefronts and one round, 37.3 with four and four rounds).
+constexpr int kFoldMaxW = 8;
 
 // value of lane (l - s) in the same 16-lane row; lanes with l % 16 < s keep `self`
 __device__ __forceinline__ float row_shr(float self, float v, int s) {
@@ -646,7 +651,8 @@ static hipError_t launch_scan_t(const S6ScanArgs& a, hipStream_t stream) {
 
 // Wavefronts per fold unit: one while a wavefront can hold every carry in one
 // round (the short path: no cross-wavefront scan, no LDS), then as many as
-// keep each at most kFoldSeg carries per round, at most 16.
+// keep each at most kFoldSeg carries per round, at most kFoldMaxW (longer
+// chains take several rounds).
 static int fold_waves(int64_t ncar) {
     int W = 1;
     while (W < kFoldMaxW && static_cast<int64_t>(W) * kFoldSeg < ncar) W *= 2;

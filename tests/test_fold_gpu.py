@@ -1,9 +1,10 @@
 """The chunk-carry combine at its structural boundaries (needs an MI355X).
 
 The combine folds each wavefront's segment of carries, scans the segment
-aggregates across lanes, and re-folds; a workgroup has 1, 2, 4, 8 or 16
+aggregates across lanes, and re-folds; a workgroup has 1, 2, 4 or 8
 wavefronts (one while 32 carries or fewer, then enough for at most 32 carries
-each), and takes the carries in rounds of up to 512.  These cases put the carry count on each side of every change,
+each), and takes the carries in rounds of up to 256.  These cases put the
+carry count on each side of every change,
 forward (folded from h0) and backward (the adjoint folded in reverse from
 dh_last), and compare with the float64 oracle.  Workgroups are placed on the
 XCD that wrote their carries when the channel blocks spread evenly over the
