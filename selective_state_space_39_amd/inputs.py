@@ -314,14 +314,17 @@ def make_workload(name: str) -> ScanInputs:
                             block=c.get("block", 64))
 
 
-def decode_params(batch: int = 256, D: int = 5120, N: int = N_STATE, seed=(SEED_ROOT, 5)):
+def decode_params(batch: int = 256, D: int = 5120, N: int = N_STATE, seed=(SEED_ROOT, 5), A_random: bool = False):
     """Channel parameters and the fp32 initial cached state for a decode run.
 
     Draw order: u (-> dt_bias), then h0 ~ N(0, 1) of shape (batch, D, N).
+    With ``A_random`` A is drawn as in ``make_scan_inputs`` (stream (*seed, 2)).
     """
     rng = np.random.default_rng(list(seed))
     A, Dskip, dt_bias = channel_params(rng, D, N)
     h0 = _normal(rng, (batch, D, N))
+    if A_random:
+        A = (-np.exp(np.random.default_rng(list(seed) + [2]).uniform(-1.5, 1.5, size=(D, N)))).astype(np.float32)
     return A, Dskip, dt_bias, h0
 
 
